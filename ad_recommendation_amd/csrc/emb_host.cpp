@@ -1,0 +1,717 @@
+// Host runtime of the embedding library: table build from a prebuilt key set, the host image that
+// is flashed to HBM in one copy per PASS, validation, write-back/export, and the C ABI.
+//
+// The table is prepared off-GPU and copied in bulk, with no insert on the device (Tencent PCG GPU
+// training talk, flash paragraph of "optimisations of each stage"); keys carry the field id in
+// their high 16 bits so all fields share one table (same talk, unified hash table paragraph).
+#include "emb.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <numeric>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "emb_internal.h"
+
+using namespace emb;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(EMB_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int n_threads() {
+  unsigned h = std::thread::hardware_concurrency();
+  if (h == 0) h = 4;
+  return (int)std::min(h, 32u);
+}
+
+// Run fn(begin, end) over [0, n) split across threads.
+template <typename Fn>
+void parallel_for(size_t n, Fn fn) {
+  const int T = n < 65536 ? 1 : n_threads();
+  if (T == 1) {
+    fn((size_t)0, n);
+    return;
+  }
+  std::vector<std::thread> th;
+  const size_t chunk = (n + T - 1) / T;
+  for (int t = 0; t < T; ++t) {
+    const size_t b = (size_t)t * chunk, e = std::min(n, b + chunk);
+    if (b >= e) break;
+    th.emplace_back([=] { fn(b, e); });
+  }
+  for (auto& x : th) x.join();
+}
+
+// fp32 -> fp16 bits, round to nearest even, subnormals kept (from the IEEE-754 binary16 format).
+uint16_t f32_to_f16(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x7F800000u) return (uint16_t)(sign | 0x7C00u | (ax > 0x7F800000u ? 0x200u : 0u));
+  const uint32_t e = ax >> 23;
+  if (e >= 113) {  // normal half range or overflow
+    uint32_t r = ((e - 112) << 10) | ((ax >> 13) & 0x3FFu);
+    const uint32_t rb = (ax >> 12) & 1u, sticky = ax & 0xFFFu;
+    if (rb && (sticky || (r & 1u))) ++r;
+    if (r >= 0x7C00u) r = 0x7C00u;
+    return (uint16_t)(sign | r);
+  }
+  if (e < 102) return (uint16_t)sign;  // below half the smallest subnormal
+  const uint32_t m = (ax & 0x7FFFFFu) | 0x800000u;
+  const int s = 126 - (int)e;  // 14..24
+  uint32_t r = m >> s;
+  const uint32_t rb = (m >> (s - 1)) & 1u, sticky = m & ((1u << (s - 1)) - 1u);
+  if (rb && (sticky || (r & 1u))) ++r;
+  return (uint16_t)(sign | r);
+}
+
+float f16_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu, x;
+  if (e == 0) {
+    if (m == 0) {
+      x = sign;
+    } else {
+      int sh = 0;
+      while (!(m & 0x400u)) { m <<= 1; ++sh; }
+      m &= 0x3FFu;
+      x = sign | ((uint32_t)(113 - sh) << 23) | (m << 13);
+    }
+  } else if (e == 31) {
+    x = sign | 0x7F800000u | (m << 13);
+  } else {
+    x = sign | ((e + 112) << 23) | (m << 13);
+  }
+  float f;
+  std::memcpy(&f, &x, 4);
+  return f;
+}
+
+struct Entry {
+  uint64_t key;
+  uint32_t home;
+  uint32_t idx;  // position in the caller's key list
+};
+
+bool entry_less(const Entry& a, const Entry& b) {
+  return a.home != b.home ? a.home < b.home : a.key < b.key;
+}
+
+// Sort by (home, key): partition by home range, then sort the parts in parallel.
+void sort_entries(std::vector<Entry>& v, uint32_t n_home) {
+  const size_t n = v.size();
+  const int T = n < 200000 ? 1 : n_threads();
+  if (T == 1) {
+    std::sort(v.begin(), v.end(), entry_less);
+    return;
+  }
+  const int P = T * 8;
+  auto part_of = [&](uint32_t h) { return (int)(((uint64_t)h * (uint64_t)P) / (uint64_t)n_home); };
+  std::vector<std::vector<size_t>> cnt(T, std::vector<size_t>(P + 1, 0));
+  const size_t chunk = (n + T - 1) / T;
+  {
+    std::vector<std::thread> th;
+    for (int t = 0; t < T; ++t)
+      th.emplace_back([&, t] {
+        const size_t b = (size_t)t * chunk, e = std::min(n, b + chunk);
+        for (size_t i = b; i < e; ++i) ++cnt[t][part_of(v[i].home)];
+      });
+    for (auto& x : th) x.join();
+  }
+  std::vector<size_t> pstart(P + 1, 0);
+  std::vector<std::vector<size_t>> pos(T, std::vector<size_t>(P, 0));
+  size_t run = 0;
+  for (int p = 0; p < P; ++p) {
+    pstart[p] = run;
+    for (int t = 0; t < T; ++t) {
+      pos[t][p] = run;
+      run += cnt[t][p];
+    }
+  }
+  pstart[P] = run;
+  std::vector<Entry> out(n);
+  {
+    std::vector<std::thread> th;
+    for (int t = 0; t < T; ++t)
+      th.emplace_back([&, t] {
+        const size_t b = (size_t)t * chunk, e = std::min(n, b + chunk);
+        for (size_t i = b; i < e; ++i) out[pos[t][part_of(v[i].home)]++] = v[i];
+      });
+    for (auto& x : th) x.join();
+  }
+  std::atomic<int> next{0};
+  {
+    std::vector<std::thread> th;
+    for (int t = 0; t < T; ++t)
+      th.emplace_back([&] {
+        for (int p; (p = next.fetch_add(1)) < P;)
+          std::sort(out.begin() + pstart[p], out.begin() + pstart[p + 1], entry_less);
+      });
+    for (auto& x : th) x.join();
+  }
+  v.swap(out);
+}
+
+}  // namespace
+
+struct EmbTable {
+  // descriptor
+  int32_t F = 0;
+  std::vector<int32_t> dim, col, gran;
+  int32_t row_dtype = EMB_F32, has_master = 0, n_tables = 1, flags = 0;
+  double lf = 0.5;
+  float acc_init = 0.f;
+  int32_t granule = 1, var_dim = 0, max_dim = 0, out_width = 0;
+  size_t elem_bytes = 4;
+  // layout
+  struct Sub {
+    uint64_t n_keys = 0, n_home = 1, n_buckets = 0, bucket_base = 0;
+    uint32_t rowref_base = 0;
+  } sub[2];
+  uint64_t n_keys = 0, total_buckets = 0, total_elems = 0;
+  uint32_t rowref_space = 0;
+  size_t off_keys = 0, off_rows = 0, off_acc = 0, off_master = 0, off_meta = 0, arena_bytes = 0;
+  uint8_t* image = nullptr;
+  bool pinned = false;
+  std::vector<uint64_t> row_keys;  // keys in rowref order
+  std::vector<uint32_t> row_ref;   // their rowrefs (ascending)
+  double mean_disp = 0;
+  uint64_t max_disp = 0;
+  // device
+  uint8_t* d_arena = nullptr;
+  bool flashed = false;
+  Timing timing;
+
+  uint64_t* keys_img() { return reinterpret_cast<uint64_t*>(image + off_keys); }
+  const uint64_t* keys_img() const { return reinterpret_cast<const uint64_t*>(image + off_keys); }
+
+  DevDesc dev() const {
+    DevDesc d{};
+    for (int t = 0; t < 2; ++t) {
+      const int s = t < n_tables ? t : 0;
+      d.tab[t].buckets = reinterpret_cast<const uint64_t*>(d_arena + off_keys) +
+                         sub[s].bucket_base * kWordsPerBucket;
+      d.tab[t].n_home = (uint32_t)sub[s].n_home;
+      d.tab[t].n_buckets = (uint32_t)sub[s].n_buckets;
+    }
+    d.n_tables = n_tables;
+    d.n_fields = F;
+    d.granule = granule;
+    d.var_dim = var_dim;
+    d.fixed_dim = dim[0];
+    d.max_dim = max_dim;
+    d.out_width = out_width;
+    d.row_f16 = row_dtype == EMB_F16;
+    d.has_master = has_master;
+    d.rows = d_arena + off_rows;
+    d.acc = reinterpret_cast<float*>(d_arena + off_acc);
+    d.master = has_master ? reinterpret_cast<float*>(d_arena + off_master) : nullptr;
+    const int32_t* meta = reinterpret_cast<const int32_t*>(d_arena + off_meta);
+    d.fdim = meta;
+    d.fcol = meta + F;
+    d.fgran = meta + 2 * F;
+    d.rowref_space = rowref_space;
+    return d;
+  }
+
+  // Host probe over the image: the same scan the device runs.
+  bool probe(uint64_t key, uint32_t* rr, int64_t* slot) const {
+    if (key == kEmpty || (int64_t)(key >> 48) >= F) return false;
+    const int t = (n_tables == 2) ? (int)(key & 1) : 0;
+    const Sub& s = sub[t];
+    const uint32_t home = home_slot(mix64(key), (uint32_t)s.n_home);
+    uint64_t b = home / kKeysPerBucket;
+    uint32_t l0 = home - (uint32_t)b * kKeysPerBucket;
+    const uint64_t* kb = keys_img() + s.bucket_base * kWordsPerBucket;
+    for (; b < s.n_buckets; ++b, l0 = 0) {
+      const uint64_t* w = kb + b * kWordsPerBucket;
+      for (uint32_t l = l0; l < (uint32_t)kKeysPerBucket; ++l) {
+        if (w[l] == key) {
+          uint32_t r = (uint32_t)w[15];
+          for (uint32_t q = 0; q < l; ++q)
+            if (w[q] != kEmpty) r += (uint32_t)gran[(int)(w[q] >> 48)];
+          *rr = r;
+          *slot = (int64_t)(b * kKeysPerBucket + l);
+          return true;
+        }
+        if (w[l] == kEmpty) return false;
+      }
+    }
+    return false;
+  }
+
+  ~EmbTable() {
+    for (auto& r : timing.pool) {
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
+    }
+    if (image) {
+      if (pinned) (void)hipHostFree(image);
+      else std::free(image);
+    }
+  }
+};
+
+extern "C" {
+
+const char* emb_last_error(void) { return g_err.c_str(); }
+
+int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys,
+                               const void* rows, const float* acc, const float* master,
+                               EmbTable** out) {
+  if (!desc || !out) return fail(EMB_EINVAL, "null descriptor or output pointer");
+  *out = nullptr;
+  if (desc->n_fields < 1 || desc->n_fields > kMaxFields)
+    return fail(EMB_EINVAL, "n_fields must be in [1, 65535]");
+  if (!desc->field_dim) return fail(EMB_EINVAL, "null field_dim");
+  if (desc->row_dtype != EMB_F32 && desc->row_dtype != EMB_F16)
+    return fail(EMB_EINVAL, "row_dtype must be EMB_F32 or EMB_F16");
+  if (desc->has_master && desc->row_dtype != EMB_F16)
+    return fail(EMB_EINVAL, "a master copy needs fp16 rows");
+  if (desc->n_tables != 1 && desc->n_tables != 2) return fail(EMB_EINVAL, "n_tables must be 1 or 2");
+  if (!(desc->load_factor > 0.0 && desc->load_factor <= 1.0))
+    return fail(EMB_EINVAL, "load_factor must be in (0, 1]");
+  if (n_keys < 0 || n_keys > 0xFFFFFFF0ll) return fail(EMB_ERANGE, "n_keys out of range");
+  if (n_keys > 0 && !keys) return fail(EMB_EINVAL, "null keys");
+
+  EmbTable* T = new (std::nothrow) EmbTable();
+  if (!T) return fail(EMB_ENOMEM, "out of host memory");
+  std::unique_ptr<EmbTable> guard(T);
+  T->F = desc->n_fields;
+  T->row_dtype = desc->row_dtype;
+  T->has_master = desc->has_master ? 1 : 0;
+  T->n_tables = desc->n_tables;
+  T->lf = desc->load_factor;
+  T->acc_init = desc->acc_init;
+  T->flags = desc->flags;
+  T->elem_bytes = desc->row_dtype == EMB_F16 ? 2 : 4;
+  T->dim.assign(desc->field_dim, desc->field_dim + desc->n_fields);
+  int g = 0;
+  int64_t width = 0;
+  for (int f = 0; f < T->F; ++f) {
+    const int d = T->dim[f];
+    if (d < 8 || d > kMaxDim || d % 8) return fail(EMB_EINVAL, "field dims must be multiples of 8 in [8, 256]");
+    g = std::gcd(g, d);
+    T->max_dim = std::max(T->max_dim, d);
+    T->col.push_back((int32_t)width);
+    width += d;
+    if (d != T->dim[0]) T->var_dim = 1;
+  }
+  if (width > (1 << 30)) return fail(EMB_ERANGE, "sum of field dims too large");
+  T->granule = g;
+  T->out_width = (int32_t)width;
+  for (int f = 0; f < T->F; ++f) T->gran.push_back(T->dim[f] / g);
+
+  // validate keys and route them to tables
+  const uint64_t* K = reinterpret_cast<const uint64_t*>(keys);
+  const size_t N = (size_t)n_keys;
+  T->n_keys = N;
+  std::atomic<int> bad{0};
+  std::vector<uint64_t> tcount(2, 0);
+  {
+    std::vector<std::vector<uint64_t>> part(64, std::vector<uint64_t>(2, 0));
+    std::atomic<int> slot{0};
+    parallel_for(N, [&](size_t b, size_t e) {
+      const int my = slot.fetch_add(1);
+      uint64_t c0 = 0, c1 = 0;
+      for (size_t i = b; i < e; ++i) {
+        const uint64_t k = K[i];
+        if (k == kEmpty) bad.store(1);
+        else if ((int64_t)(k >> 48) >= T->F) { int z = 0; bad.compare_exchange_strong(z, 2); }
+        if (T->n_tables == 2 && (k & 1)) ++c1; else ++c0;
+      }
+      part[my % 64][0] += c0;
+      part[my % 64][1] += c1;
+    });
+    for (auto& p : part) { tcount[0] += p[0]; tcount[1] += p[1]; }
+  }
+  if (bad.load() == 1) return fail(EMB_ESENTINEL, "a key equals the EMPTY marker (all bits set)");
+  if (bad.load() == 2) return fail(EMB_ERANGE, "a key's field id is >= n_fields");
+
+  // input row offsets (elements) in key order
+  std::vector<uint64_t> in_off(N + 1, 0);
+  for (size_t i = 0; i < N; ++i) in_off[i + 1] = in_off[i] + (uint64_t)T->dim[(int)(K[i] >> 48)];
+  T->total_elems = in_off[N];
+
+  // per table: homes, sort by (home, key), place, count buckets
+  std::vector<Entry> ent[2];
+  uint64_t rr_total = 0;
+  double disp_sum = 0;
+  std::vector<uint64_t> slot_of[2];
+  for (int t = 0; t < T->n_tables; ++t) {
+    EmbTable::Sub& s = T->sub[t];
+    s.n_keys = tcount[t];
+    const double nh = std::ceil((double)s.n_keys / T->lf);
+    if (nh > 4294967295.0 - 64) return fail(EMB_ERANGE, "too many home slots for one table");
+    s.n_home = std::max<uint64_t>(1, (uint64_t)nh);
+    ent[t].resize(s.n_keys);
+  }
+  {
+    size_t p0 = 0, p1 = 0;
+    for (size_t i = 0; i < N; ++i) {
+      const int t = (T->n_tables == 2 && (K[i] & 1)) ? 1 : 0;
+      Entry& en = ent[t][t ? p1++ : p0++];
+      en.key = K[i];
+      en.idx = (uint32_t)i;
+    }
+  }
+  for (int t = 0; t < T->n_tables; ++t) {
+    EmbTable::Sub& s = T->sub[t];
+    std::vector<Entry>& E = ent[t];
+    const uint32_t nh = (uint32_t)s.n_home;
+    parallel_for(E.size(), [&](size_t b, size_t e) {
+      for (size_t i = b; i < e; ++i) E[i].home = home_slot(mix64(E[i].key), nh);
+    });
+    sort_entries(E, nh);
+    for (size_t i = 1; i < E.size(); ++i)
+      if (E[i].key == E[i - 1].key) return fail(EMB_EDUPKEY, "duplicate key in the prebuilt key set");
+    slot_of[t].resize(E.size());
+    uint64_t last = 0;
+    for (size_t i = 0; i < E.size(); ++i) {
+      const uint64_t sl = i == 0 ? E[i].home : std::max<uint64_t>(E[i].home, last + 1);
+      slot_of[t][i] = sl;
+      last = sl;
+      disp_sum += (double)(sl - E[i].home);
+      T->max_disp = std::max<uint64_t>(T->max_disp, sl - E[i].home);
+    }
+    const uint64_t span = std::max<uint64_t>(s.n_home, E.empty() ? 0 : last + 1);
+    s.n_buckets = (span + kKeysPerBucket - 1) / kKeysPerBucket + 1;  // + an all-empty terminator
+    if (s.n_buckets > 0xFFFFFFF0ull) return fail(EMB_ERANGE, "table too large");
+    s.bucket_base = T->total_buckets;
+    T->total_buckets += s.n_buckets;
+    s.rowref_base = (uint32_t)rr_total;
+    for (const Entry& en : E) rr_total += (uint64_t)T->gran[(int)(en.key >> 48)];
+    if (rr_total >= 0xFFFFFFFFull) return fail(EMB_ERANGE, "rowref space exceeds 32 bits");
+  }
+  T->rowref_space = (uint32_t)rr_total;
+  T->mean_disp = N ? disp_sum / (double)N : 0.0;
+
+  // image layout = arena layout
+  const size_t eb = T->elem_bytes;
+  T->off_keys = 0;
+  T->off_rows = align256(T->total_buckets * 128);
+  T->off_acc = align256(T->off_rows + T->total_elems * eb);
+  T->off_master = align256(T->off_acc + T->total_elems * 4);
+  T->off_meta = align256(T->off_master + (T->has_master ? T->total_elems * 4 : 0));
+  T->arena_bytes = align256(T->off_meta + 3 * 4 * (size_t)T->F);
+  if (T->flags & EMB_FLAG_PINNED_STAGING) {
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&T->image), T->arena_bytes, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the host image");
+    T->pinned = true;
+  } else {
+    T->image = static_cast<uint8_t*>(std::aligned_alloc(4096, (T->arena_bytes + 4095) & ~(size_t)4095));
+    if (!T->image) return fail(EMB_ENOMEM, "host image allocation failed");
+  }
+
+  // key buckets with per-bucket rowref prefix; per key its rowref
+  uint64_t* KB = T->keys_img();
+  parallel_for(T->total_buckets * kWordsPerBucket, [&](size_t b, size_t e) {
+    std::fill(KB + b, KB + e, kEmpty);
+  });
+  T->row_keys.resize(N);
+  T->row_ref.resize(N);
+  std::vector<uint32_t> idx_by_row(N);
+  size_t rpos = 0;
+  for (int t = 0; t < T->n_tables; ++t) {
+    EmbTable::Sub& s = T->sub[t];
+    uint64_t* kb = KB + s.bucket_base * kWordsPerBucket;
+    uint64_t run = s.rowref_base;
+    uint64_t next_b = 0;  // next bucket whose prefix is still to be written
+    const std::vector<Entry>& E = ent[t];
+    for (size_t i = 0; i < E.size(); ++i) {
+      const uint64_t sl = slot_of[t][i];
+      const uint64_t b = sl / kKeysPerBucket, l = sl % kKeysPerBucket;
+      for (; next_b <= b; ++next_b) kb[next_b * kWordsPerBucket + 15] = run;
+      kb[b * kWordsPerBucket + l] = E[i].key;
+      T->row_keys[rpos] = E[i].key;
+      T->row_ref[rpos] = (uint32_t)run;
+      idx_by_row[rpos] = E[i].idx;
+      ++rpos;
+      run += (uint64_t)T->gran[(int)(E[i].key >> 48)];
+    }
+    for (; next_b < s.n_buckets; ++next_b) kb[next_b * kWordsPerBucket + 15] = run;
+  }
+
+  // rows, accumulator, master in rowref order
+  uint8_t* R = T->image + T->off_rows;
+  float* A = reinterpret_cast<float*>(T->image + T->off_acc);
+  float* M = T->has_master ? reinterpret_cast<float*>(T->image + T->off_master) : nullptr;
+  const uint8_t* rin = static_cast<const uint8_t*>(rows);
+  const int f16rows = T->row_dtype == EMB_F16;
+  parallel_for(N, [&](size_t b, size_t e) {
+    for (size_t r = b; r < e; ++r) {
+      const uint32_t i = idx_by_row[r];
+      const uint64_t D = in_off[i + 1] - in_off[i];
+      const uint64_t dst = (uint64_t)T->row_ref[r] * (uint64_t)T->granule;
+      const uint64_t src = in_off[i];
+      if (rin) {
+        std::memcpy(R + dst * eb, rin + src * eb, D * eb);
+      } else if (master && f16rows) {
+        uint16_t* h = reinterpret_cast<uint16_t*>(R) + dst;
+        for (uint64_t q = 0; q < D; ++q) h[q] = f32_to_f16(master[src + q]);
+      } else {
+        std::memset(R + dst * eb, 0, D * eb);
+      }
+      if (acc) std::memcpy(A + dst, acc + src, D * 4);
+      else std::fill(A + dst, A + dst + D, T->acc_init);
+      if (M) {
+        if (master) {
+          std::memcpy(M + dst, master + src, D * 4);
+        } else {
+          const uint16_t* h = reinterpret_cast<const uint16_t*>(R) + dst;
+          for (uint64_t q = 0; q < D; ++q) M[dst + q] = f16_to_f32(h[q]);
+        }
+      }
+    }
+  });
+  int32_t* meta = reinterpret_cast<int32_t*>(T->image + T->off_meta);
+  for (int f = 0; f < T->F; ++f) {
+    meta[f] = T->dim[f];
+    meta[T->F + f] = T->col[f];
+    meta[2 * T->F + f] = T->gran[f];
+  }
+  *out = guard.release();
+  return EMB_OK;
+}
+
+int table_info(const EmbTable* t, EmbTableInfo* info) {
+  if (!t || !info) return fail(EMB_EINVAL, "null argument");
+  std::memset(info, 0, sizeof(*info));
+  info->arena_bytes = t->arena_bytes;
+  info->key_bytes = t->total_buckets * 128;
+  info->state_bytes = t->off_meta - t->off_rows;
+  info->n_keys = t->n_keys;
+  info->total_elems = t->total_elems;
+  info->rowref_space = t->rowref_space;
+  info->granule = (uint32_t)t->granule;
+  for (int s = 0; s < t->n_tables; ++s) {
+    info->n_home[s] = t->sub[s].n_home;
+    info->n_keys_t[s] = t->sub[s].n_keys;
+    info->n_buckets[s] = t->sub[s].n_buckets;
+  }
+  info->mean_displacement = t->mean_disp;
+  info->max_displacement = t->max_disp;
+  return EMB_OK;
+}
+
+int table_device_bytes(const EmbTable* t, size_t* bytes) {
+  if (!t || !bytes) return fail(EMB_EINVAL, "null argument");
+  *bytes = t->arena_bytes;
+  return EMB_OK;
+}
+
+int pass_flash(EmbTable* t, void* d_arena, size_t arena_bytes, emb_stream_t stream) {
+  if (!t || !d_arena) return fail(EMB_EINVAL, "null table or arena");
+  if (reinterpret_cast<uintptr_t>(d_arena) % 256) return fail(EMB_EINVAL, "arena must be 256-byte aligned");
+  if (arena_bytes < t->arena_bytes) return fail(EMB_ENOSPACE, "arena smaller than table_device_bytes()");
+  hipError_t e = hipMemcpyAsync(d_arena, t->image, t->arena_bytes, hipMemcpyHostToDevice,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pass_flash copy");
+  t->d_arena = static_cast<uint8_t*>(d_arena);
+  t->flashed = true;
+  return EMB_OK;
+}
+
+int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets, int64_t n_bags,
+                    int64_t nnz, void* d_out, int32_t out_dtype, uint32_t* d_rowref,
+                    int64_t* d_slot, int64_t* d_n_miss, emb_stream_t stream) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  if (n_bags < 0 || nnz < 0 || n_bags >= (1ll << 31) || nnz >= (1ll << 31))
+    return fail(EMB_EINVAL, "n_bags and nnz must be in [0, 2^31)");
+  if (n_bags % t->F) return fail(EMB_EINVAL, "n_bags must be a multiple of n_fields");
+  if (out_dtype != EMB_F32 && out_dtype != EMB_F16) return fail(EMB_EINVAL, "bad out_dtype");
+  if (n_bags > 0 && (!d_offsets || !d_out)) return fail(EMB_EINVAL, "null offsets or output");
+  if (nnz > 0 && n_bags == 0) return fail(EMB_EINVAL, "occurrences without bags");
+  if (nnz > 0 && (!d_keys || !d_rowref)) return fail(EMB_EINVAL, "null keys or rowref");
+  if (!t->flashed) return fail(EMB_ESTATE, "lookup before pass_flash");
+  FwdLaunch a{};
+  a.d = t->dev();
+  a.keys = d_keys;
+  a.offsets = d_offsets;
+  a.n_bags = (int32_t)n_bags;
+  a.nnz = (int32_t)nnz;
+  a.out = d_out;
+  a.out_f16 = out_dtype == EMB_F16;
+  a.rowref = d_rowref;
+  a.slot = d_slot;
+  a.n_miss = reinterpret_cast<unsigned long long*>(d_n_miss);
+  LaunchCtx ctx{static_cast<hipStream_t>(stream), &t->timing};
+  hipError_t e = launch_lookup_pool(a, ctx);
+  if (e != hipSuccess) return hip_fail(e, "lookup_pool_fwd launch");
+  return EMB_OK;
+}
+
+int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* bytes) {
+  if (!t || !bytes) return fail(EMB_EINVAL, "null argument");
+  if (n_bags < 0 || nnz < 0 || nnz >= (1ll << 31)) return fail(EMB_EINVAL, "bad sizes");
+  *bytes = plan_bwd(nnz, t->rowref_space).bytes;
+  return EMB_OK;
+}
+
+int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                       int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
+                       float lr, float eps, void* d_ws, size_t ws_bytes, uint32_t* d_unique,
+                       int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  if (n_bags < 0 || nnz < 0 || n_bags >= (1ll << 31) || nnz >= (1ll << 31))
+    return fail(EMB_EINVAL, "n_bags and nnz must be in [0, 2^31)");
+  if (n_bags % t->F) return fail(EMB_EINVAL, "n_bags must be a multiple of n_fields");
+  if (grad_dtype != EMB_F32 && grad_dtype != EMB_F16) return fail(EMB_EINVAL, "bad grad_dtype");
+  if (nnz > 0 && n_bags == 0) return fail(EMB_EINVAL, "occurrences without bags");
+  if (nnz > 0 && (!d_rowref || !d_offsets || !d_grad || !d_ws))
+    return fail(EMB_EINVAL, "null rowref, offsets, grad or workspace");
+  if (d_count && !d_unique) return fail(EMB_EINVAL, "d_count needs d_unique");
+  const BwdPlan p = plan_bwd(nnz, t->rowref_space);
+  if (nnz > 0 && ws_bytes < p.bytes) return fail(EMB_ENOSPACE, "workspace smaller than bwd_workspace_bytes()");
+  if (!t->flashed) return fail(EMB_ESTATE, "backward before pass_flash");
+  BwdLaunch a{};
+  a.d = t->dev();
+  a.rowref = d_rowref;
+  a.offsets = d_offsets;
+  a.n_bags = (int32_t)n_bags;
+  a.nnz = (int32_t)nnz;
+  a.grad = d_grad;
+  a.grad_f16 = grad_dtype == EMB_F16;
+  a.lr = lr;
+  a.eps = eps;
+  a.ws = d_ws;
+  a.ws_bytes = ws_bytes;
+  a.unique = d_unique;
+  a.count = d_count;
+  a.n_unique = d_n_unique;
+  LaunchCtx ctx{static_cast<hipStream_t>(stream), &t->timing};
+  hipError_t e = launch_adagrad_bwd(a, p, ctx);
+  if (e != hipSuccess) return hip_fail(e, "sparse_adagrad_bwd launch");
+  return EMB_OK;
+}
+
+int pass_writeback(EmbTable* t, emb_stream_t stream) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  if (!t->flashed) return fail(EMB_ESTATE, "write-back before pass_flash");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n = t->off_meta - t->off_rows;
+  hipError_t e = hipMemcpyAsync(t->image + t->off_rows, t->d_arena + t->off_rows, n,
+                                hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "pass_writeback copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "pass_writeback sync");
+  return EMB_OK;
+}
+
+int table_export(const EmbTable* t, const int64_t* keys, int64_t n, void* rows, float* acc,
+                 float* master) {
+  if (!t || (n > 0 && !keys)) return fail(EMB_EINVAL, "null argument");
+  if (master && !t->has_master) return fail(EMB_EINVAL, "table keeps no master copy");
+  const size_t eb = t->elem_bytes;
+  uint64_t o = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t rr;
+    int64_t sl;
+    const uint64_t k = (uint64_t)keys[i];
+    if (!t->probe(k, &rr, &sl)) return fail(EMB_EINVAL, "table_export: key not in the table");
+    const uint64_t D = (uint64_t)t->dim[(int)(k >> 48)];
+    const uint64_t e = (uint64_t)rr * (uint64_t)t->granule;
+    if (rows) std::memcpy(static_cast<uint8_t*>(rows) + o * eb, t->image + t->off_rows + e * eb, D * eb);
+    if (acc) std::memcpy(acc + o, reinterpret_cast<const float*>(t->image + t->off_acc) + e, D * 4);
+    if (master) std::memcpy(master + o, reinterpret_cast<const float*>(t->image + t->off_master) + e, D * 4);
+    o += D;
+  }
+  return EMB_OK;
+}
+
+int table_key_rowref(const EmbTable* t, const int64_t* keys, int64_t n, uint32_t* rowref,
+                     int64_t* slot) {
+  if (!t || (n > 0 && (!keys || !rowref))) return fail(EMB_EINVAL, "null argument");
+  parallel_for((size_t)n, [&](size_t b, size_t e) {
+    for (size_t i = b; i < e; ++i) {
+      uint32_t rr = kMiss;
+      int64_t sl = -1;
+      if (!t->probe((uint64_t)keys[i], &rr, &sl)) { rr = kMiss; sl = -1; }
+      rowref[i] = rr;
+      if (slot) slot[i] = sl;
+    }
+  });
+  return EMB_OK;
+}
+
+int table_rowref_keys(const EmbTable* t, const uint32_t* rowrefs, int64_t n, int64_t* keys_out) {
+  if (!t || (n > 0 && (!rowrefs || !keys_out))) return fail(EMB_EINVAL, "null argument");
+  for (int64_t i = 0; i < n; ++i) {
+    auto it = std::lower_bound(t->row_ref.begin(), t->row_ref.end(), rowrefs[i]);
+    if (it == t->row_ref.end() || *it != rowrefs[i])
+      return fail(EMB_EINVAL, "table_rowref_keys: not a row start");
+    keys_out[i] = (int64_t)t->row_keys[(size_t)(it - t->row_ref.begin())];
+  }
+  return EMB_OK;
+}
+
+int emb_timing_enable(EmbTable* t, int enable, const char* only) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  t->timing.on = enable != 0;
+  t->timing.only = only ? only : "";
+  t->timing.used = 0;
+  return EMB_OK;
+}
+
+int emb_timing_read(EmbTable* t, char* names, size_t name_cap, int64_t* counts, double* ms,
+                    int32_t cap, int32_t* n_out) {
+  if (!t || !n_out) return fail(EMB_EINVAL, "null argument");
+  Timing& T = t->timing;
+  std::vector<std::string> nm;
+  std::vector<int64_t> cnt;
+  std::vector<double> tot;
+  for (size_t i = 0; i < T.used; ++i) {
+    Timing::Rec& r = T.pool[i];
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "timing event sync");
+    float x = 0.f;
+    e = hipEventElapsedTime(&x, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "timing elapsed");
+    size_t k = 0;
+    while (k < nm.size() && nm[k] != r.name) ++k;
+    if (k == nm.size()) { nm.push_back(r.name); cnt.push_back(0); tot.push_back(0.0); }
+    cnt[k] += 1;
+    tot[k] += x;
+  }
+  T.used = 0;
+  std::string joined;
+  for (size_t k = 0; k < nm.size(); ++k) joined += nm[k] + "\n";
+  if (names && name_cap) {
+    const size_t c = std::min(name_cap - 1, joined.size());
+    std::memcpy(names, joined.data(), c);
+    names[c] = 0;
+  }
+  const int32_t m = (int32_t)std::min<size_t>(nm.size(), (size_t)(cap > 0 ? cap : 0));
+  for (int32_t k = 0; k < m; ++k) {
+    if (counts) counts[k] = cnt[k];
+    if (ms) ms[k] = tot[k];
+  }
+  *n_out = (int32_t)nm.size();
+  return EMB_OK;
+}
+
+void table_destroy(EmbTable* t) { delete t; }
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Internal declarations shared by the host runtime (emb_host.cpp) and the gfx950 kernels
+// (emb_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+namespace emb {
+
+constexpr uint64_t kEmpty = ~0ull;             // free-slot marker in the key buckets
+constexpr int kKeysPerBucket = 15;             // 15 keys + 1 metadata word = one 128-byte line
+constexpr int kWordsPerBucket = 16;
+constexpr uint32_t kMiss = 0xFFFFFFFFu;
+constexpr uint64_t kMix = 0x9E3779B97F4A7C15ull;  // floor(2^64 / golden ratio)
+constexpr int kMaxFields = 65535;
+constexpr int kMaxDim = 256;
+
+// 64-bit key mix used to place keys; every step is invertible.
+__host__ __device__ inline uint64_t mix64(uint64_t x) {
+  x = (x ^ (x >> 32)) * kMix;
+  x = (x ^ (x >> 32)) * kMix;
+  return x ^ (x >> 32);
+}
+// Multiply-shift range reduction of the high hash half onto [0, n_home).
+__host__ __device__ inline uint32_t home_slot(uint64_t h, uint32_t n_home) {
+  return (uint32_t)(((h >> 32) * (uint64_t)n_home) >> 32);
+}
+
+// One sub-table as the kernels see it.
+struct DevTab {
+  const uint64_t* buckets;  // n_buckets * 16 words; word 15 holds the rowref prefix of the bucket
+  uint32_t n_home;
+  uint32_t n_buckets;
+};
+
+// Everything a kernel needs to reach the flashed table.
+struct DevDesc {
+  DevTab tab[2];
+  int32_t n_tables;
+  int32_t n_fields;
+  int32_t granule;     // row elements per rowref unit
+  int32_t var_dim;     // 1 when field widths differ
+  int32_t fixed_dim;   // the common width when var_dim == 0
+  int32_t max_dim;     // widest field
+  int32_t out_width;   // sum of field widths = pooled output / gradient row width
+  int32_t row_f16;
+  int32_t has_master;
+  void* rows;
+  float* acc;
+  float* master;
+  const int32_t* fdim;   // [F] width per field
+  const int32_t* fcol;   // [F] first pooled column per field
+  const int32_t* fgran;  // [F] rowref units per row of the field
+  uint32_t rowref_space; // rowref values are < rowref_space
+};
+
+// Kernel timing: events bracket each launch when enabled.
+struct Timing {
+  bool on = false;
+  std::string only;  // empty = every kernel
+  struct Rec {
+    const char* name;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pool;
+  size_t used = 0;
+};
+
+struct LaunchCtx {
+  hipStream_t stream;
+  Timing* timing;
+};
+
+// Brackets one kernel launch with events when timing is on.
+struct KTimer {
+  LaunchCtx& c;
+  Timing::Rec* r = nullptr;
+  KTimer(LaunchCtx& ctx, const char* name);
+  ~KTimer();
+};
+
+struct FwdLaunch {
+  DevDesc d;
+  const int64_t* keys;
+  const int32_t* offsets;
+  int32_t n_bags;
+  int32_t nnz;
+  void* out;
+  int32_t out_f16;
+  uint32_t* rowref;
+  int64_t* slot;
+  unsigned long long* n_miss;
+};
+
+struct BwdLaunch {
+  DevDesc d;
+  const uint32_t* rowref;
+  const int32_t* offsets;
+  int32_t n_bags;
+  int32_t nnz;
+  const void* grad;
+  int32_t grad_f16;
+  float lr, eps;
+  void* ws;
+  size_t ws_bytes;
+  uint32_t* unique;
+  int32_t* count;
+  int64_t* n_unique;
+};
+
+// Workspace carve-up for the backward (same on host and device side).
+struct BwdPlan {
+  int32_t n;           // items (occurrences)
+  int32_t tiles;       // sort tiles
+  int32_t passes;      // 8-bit radix passes
+  uint32_t miss_key;   // key given to missed occurrences (sorts last)
+  size_t off_ka, off_va, off_kb, off_vb, off_counts, off_tot, off_ctr, off_long, off_seg;
+  size_t bytes;
+};
+BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space);
+
+// Launchers (emb_kernels.hip).  Each returns hipSuccess or the launch error.
+hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx);
+hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ctx);
+
+}  // namespace emb

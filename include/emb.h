@@ -1,0 +1,204 @@
+/*
+ * mi355emb -- one training step of a GPU-resident sparse embedding layer on MI355X (gfx950).
+ *
+ * The step the library runs, and where each part is described:
+ *   - A unified, insert-free hash table.  Keys are int64 with the raw id in the low 48 bits and the
+ *     field (table) id in the high 16 bits, so all fields share one table and one kernel serves the
+ *     lookup and one the update (Tencent PCG GPU training talk, "compute optimisation", unified
+ *     hash table paragraph).  The table is prepared off-GPU and copied to HBM in one piece per PASS;
+ *     there is no insert (same talk, flash paragraph of "optimisations of each stage").  Optionally
+ *     split in two tables by key parity ("Multiple Hash") with per-field row widths ("dynamic
+ *     embedding") (same talk, space optimisation).
+ *   - Forward: probe every key of a CSR batch and sum-pool each bag, as EmbeddingBag(mode='sum')
+ *     over flat ids and offsets (JD ads article, section 4.2.1).
+ *   - Backward: deduplicate the touched rows, reduce each row's gradient over its occurrences, and
+ *     apply element-wise sparse Adagrad to those rows only; untouched rows and state stay as they
+ *     are (JD ads article, section 3.2.1), with fp16 rows, an fp32 master copy for the update and
+ *     fp32 optimizer state (JD ads article, sections 3.2.3 and 5.2).
+ *
+ * Conventions for every function:
+ *   - Return value: 0 (EMB_OK) or a negative emb_status.  Nothing throws.  emb_last_error() gives a
+ *     thread-local message for the last failure on the calling thread.
+ *   - "d_" pointers are device pointers (HBM), owned by the caller; the hot-path entry points never
+ *     allocate device memory.  Host pointers passed to a function are only read during the call.
+ *   - Device work is enqueued on the caller's stream (a hipStream_t passed as void*, NULL = the null
+ *     stream) and is asynchronous unless a function says it synchronises.
+ *   - A table object is not thread-safe; distinct tables are independent.
+ */
+#ifndef MI355EMB_H
+#define MI355EMB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct EmbTable EmbTable; /* opaque; created and destroyed by the library */
+typedef void* emb_stream_t;       /* a hipStream_t */
+
+typedef enum { EMB_F32 = 0, EMB_F16 = 1 } emb_dtype;
+
+typedef enum {
+  EMB_OK = 0,
+  EMB_EINVAL = -1,     /* bad argument: null pointer, bad size, bad descriptor field */
+  EMB_EDUPKEY = -2,    /* the prebuilt key set holds a key twice */
+  EMB_ESENTINEL = -3,  /* a prebuilt key equals the EMPTY marker (all 64 bits set) */
+  EMB_ERANGE = -4,     /* a field id >= n_fields, or a size beyond a documented limit */
+  EMB_ENOSPACE = -5,   /* arena or workspace smaller than required */
+  EMB_ESTATE = -6,     /* call out of order, e.g. lookup before pass_flash */
+  EMB_EHIP = -7,       /* a HIP runtime call failed; the HIP error text is in emb_last_error() */
+  EMB_ENOMEM = -8      /* host allocation failed */
+} emb_status;
+
+/* Marker stored in rowref for an occurrence that found no row. */
+#define EMB_ROWREF_MISS 0xFFFFFFFFu
+
+/* Table flags. */
+#define EMB_FLAG_PINNED_STAGING 1 /* keep the host image in pinned memory (needs a GPU at create) */
+
+typedef struct {
+  int32_t n_fields;          /* F, 1..65535; field id 0xFFFF is reserved for the EMPTY marker */
+  const int32_t* field_dim;  /* F row widths, each a multiple of 8 in [8, 256] */
+  int32_t row_dtype;         /* EMB_F32 or EMB_F16 */
+  int32_t has_master;        /* 1: keep an fp32 master copy beside fp16 rows (EMB_F16 only) */
+  int32_t n_tables;          /* 1: one unified table; 2: two tables, a key lives in table (key & 1) */
+  double load_factor;        /* in (0, 1]; each table gets ceil(N_t / load_factor) home slots */
+  float acc_init;            /* Adagrad accumulator start value when no accumulator is supplied */
+  int32_t flags;             /* EMB_FLAG_* */
+} EmbTableDesc;
+
+typedef struct {
+  uint64_t arena_bytes;      /* device bytes pass_flash needs */
+  uint64_t key_bytes;        /* of which the probed key buckets */
+  uint64_t state_bytes;      /* of which rows + accumulator + master */
+  uint64_t n_keys;
+  uint64_t total_elems;      /* row elements over all keys */
+  uint32_t rowref_space;     /* rowref values run over [0, rowref_space) */
+  uint32_t granule;          /* row elements per rowref unit */
+  uint64_t n_home[2];        /* home slots per table */
+  uint64_t n_keys_t[2];      /* keys per table */
+  uint64_t n_buckets[2];     /* 128-byte buckets per table */
+  double mean_displacement;  /* mean of (slot - home) over all keys */
+  uint64_t max_displacement;
+} EmbTableInfo;
+
+/*
+ * Build the table from a prebuilt key set (the PASS's deduplicated keys) and each key's row and
+ * optimizer state.  Host only: no device work.
+ *   keys   : n_keys int64 keys, any order.  Must be distinct (EMB_EDUPKEY), never all-ones
+ *            (EMB_ESENTINEL), with field id (key >> 48) < n_fields (EMB_ERANGE).
+ *   rows   : row data packed in key order; key i contributes field_dim[field(key i)] elements of
+ *            row_dtype.  NULL: rows start at zero, or at fp16(master) when master is given.
+ *   acc    : fp32, same packing as rows.  NULL: every element starts at desc->acc_init.
+ *   master : fp32, same packing (fp16 tables with has_master only).  NULL: master = fp32(row).
+ * Layout (ordered linear probing in 128-byte buckets of 15 keys; rows stored in slot order) is a
+ * pure function of the key set.  The inputs are copied; the caller may free them on return.
+ */
+int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys,
+                               const void* rows, const float* acc, const float* master,
+                               EmbTable** out);
+
+/* Sizes and builder statistics of a table (host only). */
+int table_info(const EmbTable* t, EmbTableInfo* info);
+
+/* Device bytes pass_flash needs in its arena (host only). */
+int table_device_bytes(const EmbTable* t, size_t* bytes);
+
+/*
+ * Copy the whole prebuilt table (key buckets, rows, accumulator, master, field metadata) into the
+ * caller's device arena in one bulk host-to-device copy, enqueued on `stream`.  The arena must be
+ * 256-byte aligned and at least table_device_bytes() long (EMB_ENOSPACE).  The arena stays bound
+ * to the table until the next pass_flash or table_destroy; rowrefs from an earlier flash are
+ * invalid afterwards.  With a pageable host image the copy is synchronous with respect to the host.
+ */
+int pass_flash(EmbTable* t, void* d_arena, size_t arena_bytes, emb_stream_t stream);
+
+/*
+ * Forward: one launch probes every key and sum-pools every bag.
+ *   d_keys    : nnz int64 keys of the CSR batch.
+ *   d_offsets : n_bags + 1 int32 offsets, offsets[0] = 0, non-decreasing, offsets[n_bags] = nnz.
+ *               Bag j belongs to sample j / F and field j % F (sample-major); n_bags % F == 0.
+ *   d_out     : [n_bags / F, sum_f field_dim[f]] of out_dtype, row-major; field f of sample b is
+ *               written at columns [sum_{f'<f} field_dim[f'], + field_dim[f]).  Every element is
+ *               written (an empty bag gives zeros).  Sums are taken in fp32 and rounded once.
+ *   d_rowref  : nnz uint32, the row each occurrence resolved to (EMB_ROWREF_MISS when the key is
+ *               absent, is the EMPTY marker, or has a field id other than its bag's field).  This is
+ *               the state sparse_adagrad_bwd consumes; it is valid until the next pass_flash.
+ *   d_slot    : nullable; nnz int64 logical slot of each occurrence in its table (-1 on a miss).
+ *   d_n_miss  : nullable; one int64 to which the number of missed occurrences is added.
+ * A miss adds nothing to its bag.  Errors: EMB_ESTATE before pass_flash; EMB_EINVAL on null
+ * required pointers, n_bags % F != 0, nnz < 0 or n_bags/nnz >= 2^31.
+ */
+int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets, int64_t n_bags,
+                    int64_t nnz, void* d_out, int32_t out_dtype, uint32_t* d_rowref,
+                    int64_t* d_slot, int64_t* d_n_miss, emb_stream_t stream);
+
+/* Device workspace bytes sparse_adagrad_bwd needs for a batch of this shape (host only). */
+int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* bytes);
+
+/*
+ * Backward + update: deduplicate the rows named by d_rowref, sum each row's upstream-gradient
+ * slices over its occurrences (a key repeated inside a bag counts every time), and apply sparse
+ * Adagrad to each touched element:
+ *     acc += g*g;   delta = lr * g / (sqrt(acc) + eps)   (the new acc)
+ *     fp32 rows: w -= delta;  fp16 rows with master: master -= delta, row = fp16(master);
+ *     fp16 rows without master: row = fp16(fp32(row) - delta).
+ * Rows, accumulators and masters that no occurrence names are not touched.
+ *   d_rowref, d_offsets, n_bags, nnz : as produced for / by lookup_pool_fwd on this flash.
+ *   d_grad     : upstream gradient, same shape and layout as the forward output, grad_dtype.
+ *   d_ws       : workspace of at least bwd_workspace_bytes(n_bags, nnz) (EMB_ENOSPACE); its
+ *                contents need no initialisation.
+ *   d_unique   : nullable; receives the U distinct touched rowrefs in ascending order, which is
+ *                ascending (table, slot) order.  Needs room for min(nnz, rows) entries.
+ *   d_count    : nullable (only with d_unique); occurrence count of each unique rowref.
+ *   d_n_unique : nullable; receives U (int64).
+ * The gradient reduction and the update run in a fixed order, so results are reproducible run to
+ * run.  Errors as for lookup_pool_fwd.
+ */
+int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                       int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
+                       float lr, float eps, void* d_ws, size_t ws_bytes, uint32_t* d_unique,
+                       int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream);
+
+/*
+ * Copy rows, accumulators and masters from the device arena back into the table's host image
+ * (the end-of-PASS write-back).  Synchronises `stream`.
+ */
+int pass_writeback(EmbTable* t, emb_stream_t stream);
+
+/*
+ * Read the host image by key: for each of the n keys, write its row (row_dtype, packed with the
+ * width of the key's field), accumulator and master (each pointer nullable) -- the state as of the
+ * last pass_writeback, or as built when none happened.  A key not in the table gives EMB_EINVAL.
+ */
+int table_export(const EmbTable* t, const int64_t* keys, int64_t n, void* rows, float* acc,
+                 float* master);
+
+/* Host-side lookup of n keys: rowref (EMB_ROWREF_MISS if absent) and logical slot (-1). */
+int table_key_rowref(const EmbTable* t, const int64_t* keys, int64_t n, uint32_t* rowref,
+                     int64_t* slot);
+
+/* Key of each rowref (host).  An invalid rowref gives EMB_EINVAL. */
+int table_rowref_keys(const EmbTable* t, const uint32_t* rowrefs, int64_t n, int64_t* keys_out);
+
+/*
+ * Kernel timing.  With timing on, each kernel launch of this table (or only those named `only`,
+ * when it is not NULL) is bracketed by HIP events on the stream it runs on.  emb_timing_read
+ * synchronises those events and reports, per kernel name, the number of launches and the summed
+ * milliseconds since the last read, then resets.
+ *   names  : buffer of name_cap bytes receiving '\n'-separated kernel names.
+ *   counts, ms : arrays of cap entries.  *n_out receives the number of kernel names.
+ */
+int emb_timing_enable(EmbTable* t, int enable, const char* only);
+int emb_timing_read(EmbTable* t, char* names, size_t name_cap, int64_t* counts, double* ms,
+                    int32_t cap, int32_t* n_out);
+
+void table_destroy(EmbTable* t);
+const char* emb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MI355EMB_H */

@@ -1,0 +1,160 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, builds the same table
+layout as the oracle (bit-exact slots), and rejects bad input with the documented codes.  No
+device work runs here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from ad_recommendation_amd import emb
+from gen import synth, workloads as W
+from oracle import emb_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "emb.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = emb.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(emb.exported_symbols()) == set(names)
+
+
+def _table(w, **kw):
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    T = emb.Table(synth.field_dims(w), emb.EMB_F16 if w.row_dtype == "f16" else emb.EMB_F32,
+                  w.has_master, w.n_tables, w.load_factor, w.acc_init, keys, rows, None, master,
+                  **kw)
+    return T, keys, rows, master
+
+
+@pytest.mark.parametrize("w", [W.TINY, W.scaled(W.F26, n_keys=300_000, batch=64),
+                               W.scaled(W.F40_VARDIM, n_keys=400_000, batch=64),
+                               W.scaled(W.F100, n_keys=200_000, batch=16)])
+def test_layout_slots_bit_exact_with_oracle(w):
+    T, keys, rows, master = _table(w)
+    ot = O.Table(keys, synth.field_dims(w), w.row_dtype, w.has_master, w.n_tables, w.load_factor,
+                 w.acc_init, rows, master=master)
+    rr, sl = emb.table_key_rowref(T.h, keys)
+    assert np.array_equal(sl, ot.slot)
+    assert T.info["n_home"][:w.n_tables] == ot.n_home
+    # rowrefs: ascending in (table, slot); distinct; map back to their keys
+    order = np.lexsort((ot.slot, ot.tab))
+    assert np.all(np.diff(rr[order].astype(np.int64)) > 0)
+    assert np.array_equal(emb.table_rowref_keys(T.h, rr), keys.view(np.int64))
+    # the host image holds every key's initial row and state
+    sample = keys[:: max(1, keys.size // 500)]
+    r2, a2, m2 = T.export(sample)
+    idx = ot.key_index(sample)
+    want_r = np.concatenate([ot.state_of(int(i))[0] for i in idx])
+    assert r2.tobytes() == want_r.tobytes()
+    assert np.all(a2 == np.float32(w.acc_init))
+    if w.has_master:
+        assert m2.tobytes() == np.concatenate([ot.state_of(int(i))[2] for i in idx]).tobytes()
+    assert abs(T.info["mean_displacement"] - (ot.slot - ot.home).mean()) < 1e-9
+
+
+def test_absent_keys_miss_on_host_probe():
+    T, keys, _, _ = _table(W.TINY)
+    absent = (keys[:100] ^ np.uint64(1 << 47))
+    rr, sl = emb.table_key_rowref(T.h, absent)
+    assert np.all(rr == emb.ROWREF_MISS) and np.all(sl == -1)
+    rr, sl = emb.table_key_rowref(T.h, np.array([-1], dtype=np.int64))
+    assert rr[0] == emb.ROWREF_MISS
+
+
+def _err(fn, *a, **k):
+    with pytest.raises(emb.EmbError) as e:
+        fn(*a, **k)
+    return e.value.name
+
+
+def test_create_errors():
+    k = np.arange(1, 101, dtype=np.int64)
+    r = np.zeros(100 * 8, dtype=np.float32)
+    mk = emb.table_create_from_prebuilt
+    assert _err(mk, [8], emb.EMB_F32, False, 1, 0.5, 0.1, np.r_[k, k[:1]], np.zeros(101 * 8, np.float32)) == "EMB_EDUPKEY"
+    assert _err(mk, [8], emb.EMB_F32, False, 1, 0.5, 0.1, np.r_[k, [-1]], np.zeros(101 * 8, np.float32)) == "EMB_ESENTINEL"
+    assert _err(mk, [8], emb.EMB_F32, False, 1, 0.5, 0.1, np.r_[k, [(1 << 48) | 3]], np.zeros(101 * 8, np.float32)) == "EMB_ERANGE"
+    assert _err(mk, [8], emb.EMB_F32, False, 1, 0.0, 0.1, k, r) == "EMB_EINVAL"
+    assert _err(mk, [8], emb.EMB_F32, False, 1, 1.5, 0.1, k, r) == "EMB_EINVAL"
+    assert _err(mk, [12], emb.EMB_F32, False, 1, 0.5, 0.1, k, None) == "EMB_EINVAL"
+    assert _err(mk, [512], emb.EMB_F32, False, 1, 0.5, 0.1, k, None) == "EMB_EINVAL"
+    assert _err(mk, [8], emb.EMB_F32, True, 1, 0.5, 0.1, k, r) == "EMB_EINVAL"
+    assert _err(mk, [8], emb.EMB_F32, False, 3, 0.5, 0.1, k, r) == "EMB_EINVAL"
+    # null key pointer with a positive count
+    d = (ctypes.c_int32 * 1)(8)
+    desc = emb.EmbTableDesc(1, d, 0, 0, 1, 0.5, 0.1, 0)
+    h = ctypes.c_void_p()
+    assert emb.lib().table_create_from_prebuilt(ctypes.byref(desc), None, 5, None, None, None,
+                                                ctypes.byref(h)) == -1
+
+
+def test_rows_null_and_master_from_rows():
+    k = (np.arange(1, 51, dtype=np.int64))
+    T = emb.Table([8], emb.EMB_F32, False, 1, 0.5, 0.25, k)
+    r, a, _ = T.export(k[:3])
+    assert np.all(r == 0) and np.all(a == np.float32(0.25))
+    rows16 = (np.arange(50 * 8) % 7 - 3).astype(np.float16) / np.float16(8)
+    T2 = emb.Table([8], emb.EMB_F16, True, 1, 0.5, 0.1, k, rows16)
+    r, a, m = T2.export(k)
+    assert r.tobytes() == rows16.tobytes() and m.tobytes() == rows16.astype(np.float32).tobytes()
+    master = np.random.default_rng(0).standard_normal(50 * 8).astype(np.float32)
+    T3 = emb.Table([8], emb.EMB_F16, True, 1, 0.5, 0.1, k, None, None, master)
+    r, a, m = T3.export(k)
+    assert r.tobytes() == master.astype(np.float16).tobytes()      # fp16 RNE of the master copy
+    assert m.tobytes() == master.tobytes()
+
+
+def test_host_fp16_rounding_matches_numpy_on_hard_cases():
+    vals = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -24, 2 ** -25, 3 * 2 ** -26, 2 ** -14 - 2 ** -26,
+                     65504, 65520, 65519.99, -0.0, 6.1e-5, 5.96e-8, 1e-9, -2.5e-6], dtype=np.float32)
+    k = np.arange(1, 3, dtype=np.int64)
+    m = np.zeros(16, dtype=np.float32)
+    m[:vals.size] = vals
+    T = emb.Table([8], emb.EMB_F16, True, 1, 0.5, 0.1, k, None, None, m)
+    r, _, _ = T.export(k)
+    with np.errstate(over="ignore"):
+        assert r.tobytes() == m.astype(np.float16).tobytes()
+
+
+def test_call_errors_without_device_work():
+    T, keys, _, _ = _table(W.TINY)
+    L = emb.lib()
+    nul = None
+    # lookup arguments are checked before the table state
+    assert L.lookup_pool_fwd(T.h, 8, 8, 4, 4, 8, 7, 8, nul, nul, nul) == -1       # bad out dtype
+    assert L.lookup_pool_fwd(T.h, nul, 8, 4, 4, 8, 0, 8, nul, nul, nul) == -1     # null keys
+    assert L.lookup_pool_fwd(T.h, 8, 8, -1, 4, 8, 0, 8, nul, nul, nul) == -1      # negative size
+    assert L.lookup_pool_fwd(T.h, 8, 8, 4, 4, 8, 0, 8, nul, nul, nul) == -6       # before flash
+    assert L.sparse_adagrad_bwd(T.h, 8, 8, 4, 4, 8, 0, 0.1, 1e-8, 8, 16, nul, nul, nul, nul) == -5  # ws too small
+    assert L.sparse_adagrad_bwd(T.h, 8, 8, 4, 4, 8, 0, 0.1, 1e-8, 8, 1 << 20, nul, 8, nul, nul) == -1  # count w/o unique
+    assert L.sparse_adagrad_bwd(T.h, 8, 8, 4, 4, 8, 0, 0.1, 1e-8, 8, 1 << 20, nul, nul, nul, nul) == -6
+    assert L.pass_flash(T.h, 256, 16, nul) == -5                                    # arena too small
+    assert L.pass_flash(T.h, 100, 1 << 40, nul) == -1                               # misaligned
+    assert L.pass_writeback(T.h, nul) == -6
+    assert emb.lib().emb_last_error()
+
+
+def test_multifield_bag_count_must_divide():
+    w = W.scaled(W.F26, n_keys=26_000, batch=4)
+    T, _, _, _ = _table(w)
+    assert emb.lib().lookup_pool_fwd(T.h, 8, 8, 27, 4, 8, 0, 8, None, None, None) == -1
+
+
+def test_workspace_size_grows_with_batch():
+    T, _, _, _ = _table(W.TINY)
+    a = emb.bwd_workspace_bytes(T.h, 256, 1024)
+    b = emb.bwd_workspace_bytes(T.h, 256 * 64, 1024 * 64)
+    assert 0 < a < b and b >= 16 * 1024 * 64

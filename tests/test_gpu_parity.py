@@ -1,0 +1,250 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle on the same seeded
+inputs.  Bit-exact for slots, rowrefs (as keys), miss counts, the unique set and its counts;
+within the derived tolerances for pooled output and the updated rows, accumulators and masters
+over several consecutive steps (each step's forward sees the previous step's update)."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from ad_recommendation_amd import emb  # noqa: E402
+from gen import synth, workloads as W  # noqa: E402
+from oracle import emb_oracle as O  # noqa: E402
+from tests import parity_util as P  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": emb.EMB_F32, "f16": emb.EMB_F16}
+TDT = {"f32": torch.float32, "f16": torch.float16}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    emb.lib()
+    yield
+
+
+def gpu_table(w, keys, rows, master, dims):
+    T = emb.Table(dims, DT[w.row_dtype], w.has_master, w.n_tables, w.load_factor, w.acc_init,
+                  keys, rows, None, master)
+    T.flash()
+    return T
+
+
+def gpu_step(T, keys, offsets, grad, out_dtype, grad_dtype, lr, eps, want_unique=True):
+    dev = "cuda"
+    F = T.n_fields
+    k = torch.from_numpy(np.ascontiguousarray(keys)).to(dev)
+    o = torch.from_numpy(np.ascontiguousarray(offsets, dtype=np.int32)).to(dev)
+    n_bags, nnz = o.numel() - 1, k.numel()
+    out = torch.full((n_bags // F, T.out_width), float("nan"), dtype=TDT[out_dtype], device=dev)
+    rowref = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    slot = torch.empty(max(nnz, 1), dtype=torch.int64, device=dev)
+    n_miss = torch.zeros(1, dtype=torch.int64, device=dev)
+    emb.lookup_pool_fwd(T.h, k, o, n_bags, nnz, out, DT[out_dtype], rowref, slot, n_miss)
+    g = torch.from_numpy(np.ascontiguousarray(grad)).to(dev)
+    ws = torch.empty(max(1, emb.bwd_workspace_bytes(T.h, n_bags, nnz)), dtype=torch.uint8, device=dev)
+    uniq = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev) if want_unique else None
+    cnt = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev) if want_unique else None
+    nu = torch.full((1,), -1, dtype=torch.int64, device=dev)
+    emb.sparse_adagrad_bwd(T.h, rowref, o, n_bags, nnz, g, DT[grad_dtype], lr, eps, ws, uniq, cnt, nu)
+    torch.cuda.synchronize()
+    U = int(nu.item())
+    res = {
+        "out": out.cpu().numpy(),
+        "rowref": rowref.cpu().numpy().view(np.uint32)[:nnz],
+        "slot": slot.cpu().numpy()[:nnz],
+        "n_miss": int(n_miss.item()),
+        "n_unique": U,
+    }
+    if want_unique:
+        res["unique"] = uniq.cpu().numpy().view(np.uint32)[:U]
+        res["count"] = cnt.cpu().numpy()[:U]
+    return res
+
+
+def run_parity(w, steps=3, batches=None, lr=None, eps=None, check_all_keys=True):
+    """Run `steps` GPU steps and the oracle side by side; check every output."""
+    dims = synth.field_dims(w)
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    say(f"[parity] {w.name}: {keys.size} keys, building")
+    T = gpu_table(w, keys, rows, master, dims)
+    ot = P.oracle_table(w, keys, rows, master, dims)
+    bud = P.Budget(ot)
+    lr = w.lr if lr is None else lr
+    eps = w.eps if eps is None else eps
+    touched_keys = set()
+    for s in range(steps):
+        bt = batches[s] if batches is not None else synth.batch(w, s)
+        kk, off, grad = bt["keys"], bt["offsets"], bt["grad"]
+        say(f"[parity] {w.name} step {s}: nnz={kk.size}")
+        res = gpu_step(T, kk, off, grad, w.out_dtype, w.grad_dtype, lr, eps)
+        # forward: slots and rowrefs bit-exact, miss count exact, pooled within tolerance
+        kidx, tab, slot = ot.lookup(kk, off)
+        assert np.array_equal(res["slot"], slot)
+        hit = kidx >= 0
+        assert np.all(res["rowref"][~hit] == emb.ROWREF_MISS)
+        if hit.any():
+            assert np.array_equal(emb.table_rowref_keys(T.h, res["rowref"][hit]),
+                                  kk[hit].view(np.int64))
+        assert res["n_miss"] == int((~hit).sum())
+        out_o, nm = ot.forward(kk, off, w.out_dtype)
+        assert nm == res["n_miss"]
+        assert not np.isnan(res["out"].astype(np.float64)).any()
+        P.check_pooled(res["out"], out_o, P.pooled_scale(ot, kk, off, bud), w.out_dtype)
+        # backward: unique set (ascending (table, slot)) and counts bit-exact
+        u, utab, uslot, ucnt = bud.oracle_step(ot, kk, off, grad, lr, eps)
+        assert res["n_unique"] == u.size
+        got_keys = emb.table_rowref_keys(T.h, res["unique"]) if u.size else np.zeros(0, np.int64)
+        assert np.array_equal(got_keys.view(np.uint64), ot.keys[u])
+        assert np.array_equal(res["count"], ucnt)
+        assert np.all(np.diff(res["unique"].astype(np.int64)) > 0)
+        touched_keys.update(ot.keys[u].tolist())
+    emb.pass_writeback(T.h)
+    sel = ot.keys if check_all_keys else np.array(sorted(touched_keys), dtype=np.uint64)
+    r, a, m = T.export(sel)
+    P.check_state(ot, bud, sel, r, a, m)
+    say(f"[parity] {w.name}: ok")
+    T.close()
+
+
+def test_tiny_three_steps():
+    run_parity(W.TINY, steps=3)
+
+
+def test_f26_full_size_three_steps():
+    # the 26-field, 4M-key, batch-4096 workload at full size
+    run_parity(W.F26, steps=3, check_all_keys=False)
+
+
+def test_f100_fp16_master_scaled():
+    run_parity(W.scaled(W.F100, n_keys=2_000_000, batch=1024), steps=3, check_all_keys=False)
+
+
+def test_f40_vardim_two_tables_scaled():
+    run_parity(W.scaled(W.F40_VARDIM, n_keys=2_000_000, batch=2048), steps=3, check_all_keys=False)
+
+
+def test_f64_fp16_no_master_scaled():
+    run_parity(W.scaled(W.F64_PASS, n_keys=1_000_000, batch=1024), steps=3, check_all_keys=False)
+
+
+# ------------------------------------------------------------------ edge cases
+def _edge_batches(w, keys, F):
+    """Hand-made CSR batches: empty bags, repeats inside a bag, misses, the EMPTY key, one key
+    for every occurrence (a segment far longer than one block's share), and a ragged tail."""
+    r = np.random.default_rng(5)
+    width = int(synth.field_dims(w).sum())
+    fk = [keys[(keys >> np.uint64(48)) == np.uint64(0 if w.field0_only else f)] for f in range(F)]
+    out = []
+    # 1) mixed: empty bags, repeated key, absent key, EMPTY key
+    bags = []
+    for j in range(64 * F):
+        f = j % F
+        kind = j % 7
+        if kind == 0:
+            bags.append([])
+        elif kind == 1:
+            bags.append([fk[f][3]] * 5)
+        elif kind == 2:
+            bags.append([fk[f][r.integers(fk[f].size)] ^ np.uint64(1 << 47)])
+        elif kind == 3:
+            bags.append([np.uint64(O.EMPTY), fk[f][1]])
+        else:
+            bags.append(list(fk[f][r.integers(0, fk[f].size, size=r.integers(1, 9))]))
+    out.append(bags)
+    # 2) one key everywhere: 9000 occurrences of a single row of field 0
+    bags = [[fk[j % F][0]] * (1 if j % F else 600) for j in range(15 * F)]
+    out.append(bags)
+    res = []
+    for bags in out:
+        lens = np.array([len(b) for b in bags], dtype=np.int64)
+        off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        kk = np.array([k for b in bags for k in b], dtype=np.uint64).view(np.int64)
+        B = len(bags) // F
+        g = r.standard_normal((B, width)).astype(np.float16 if w.grad_dtype == "f16" else np.float32)
+        res.append({"keys": kk, "offsets": off, "grad": g})
+    return res
+
+
+@pytest.mark.parametrize("w", [W.TINY, W.scaled(W.F40_VARDIM, n_keys=100_000, batch=16),
+                               W.scaled(W.F64_PASS, n_keys=64_000, batch=16)])
+def test_edge_batches(w):
+    keys = synth.resident_keys(w)
+    run_parity(w, steps=2, batches=_edge_batches(w, keys, w.n_fields))
+
+
+def test_zero_gradient_leaves_rows_bit_identical():
+    w = W.scaled(W.F100, n_keys=20_000, batch=64)
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    T = gpu_table(w, keys, rows, master, synth.field_dims(w))
+    bt = synth.batch(w, 0)
+    res = gpu_step(T, bt["keys"], bt["offsets"], np.zeros_like(bt["grad"]), "f16", "f16", 0.05, 1e-8)
+    assert res["n_unique"] > 0
+    emb.pass_writeback(T.h)
+    r, a, m = T.export(keys)
+    assert r.tobytes() == rows.tobytes() and m.tobytes() == master.tobytes()
+    assert np.all(a == np.float32(w.acc_init))
+
+
+def test_fp16_subnormal_rows_and_tiny_updates():
+    w = W.scaled(W.F64_PASS, n_keys=6_400, batch=32)
+    keys = synth.resident_keys(w)
+    dims = synth.field_dims(w)
+    r = np.random.default_rng(9)
+    rows = (r.standard_normal(keys.size * 32) * 2.0 ** -18).astype(np.float16)  # mostly subnormal
+    T = gpu_table(w, keys, rows, None, dims)
+    ot = P.oracle_table(w, keys, rows, None, dims)
+    bud = P.Budget(ot)
+    bt = synth.batch(w, 0)
+    g = (bt["grad"].astype(np.float32) * 1e-3).astype(np.float16)
+    res = gpu_step(T, bt["keys"], bt["offsets"], g, "f16", "f16", 1e-4, 1e-8)
+    out_o, _ = ot.forward(bt["keys"], bt["offsets"], "f16")
+    P.check_pooled(res["out"], out_o, P.pooled_scale(ot, bt["keys"], bt["offsets"]), "f16")
+    bud.oracle_step(ot, bt["keys"], bt["offsets"], g, 1e-4, 1e-8)
+    emb.pass_writeback(T.h)
+    rr, a, m = T.export(keys)
+    P.check_state(ot, bud, keys, rr, a, m)
+
+
+def test_single_key_table_and_empty_batch():
+    w = W.scaled(W.TINY, n_keys=1, batch=4)
+    keys = synth.resident_keys(w)
+    rows, _ = synth.initial_state(w)
+    dims = synth.field_dims(w)
+    T = gpu_table(w, keys, rows, None, dims)
+    # empty batch: zero occurrences over 4 bags
+    res = gpu_step(T, np.zeros(0, np.int64), np.zeros(5, np.int32), np.ones((4, 16), np.float32),
+                   "f32", "f32", 0.05, 1e-8)
+    assert np.all(res["out"] == 0) and res["n_unique"] == 0 and res["n_miss"] == 0
+    bt = {"keys": np.repeat(keys.view(np.int64), 7), "offsets": np.array([0, 0, 3, 7, 7], np.int32),
+          "grad": np.ones((4, 16), np.float32)}
+    run_parity(w, steps=2, batches=[bt, bt])
+
+
+def test_integer_outputs_are_deterministic():
+    w = W.scaled(W.F26, n_keys=260_000, batch=2048)
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    dims = synth.field_dims(w)
+    bt = synth.batch(w, 0)
+    outs = []
+    for rep in range(3):
+        T = gpu_table(w, keys, rows, master, dims)
+        res = gpu_step(T, bt["keys"], bt["offsets"], bt["grad"], "f32", "f32", 0.05, 1e-8)
+        emb.pass_writeback(T.h)
+        st = T.export(keys[:5000])
+        outs.append((res["rowref"].tobytes(), res["unique"].tobytes(), res["count"].tobytes(),
+                     res["out"].tobytes(), st[0].tobytes(), st[1].tobytes()))
+        T.close()
+    assert outs[0] == outs[1] == outs[2]
