@@ -1,0 +1,294 @@
+"""Benchmark of one training step of the GPU-resident embedding layer (forward probe + sum pool,
+backward dedup + segmented gradient reduction + sparse Adagrad) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload f26|tiny|f100|f40|f64]
+
+Prints one JSON line: rows looked up + updated per second over K timed steps (inputs resident in
+HBM, a ring of distinct synthetic batches cycled in order so each step sees the previous step's
+update), the roofline of the dominant kernel (algorithmic bytes per launch / its event-timed
+duration, against 8 TB/s), and the CPU oracle's rate on a bounded sample as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "embedding rows looked up+updated/sec (fwd+bwd) and achieved HBM GB/s vs peak"
+LONG_SEGMENT = 32          # occurrences above which a row takes the library's block path
+KERNEL_SRC = os.path.join(ROOT, "ad_recommendation_amd", "csrc", "emb_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_src_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------- byte model
+def batch_stats(w, bt, dims):
+    """Per-batch counts the byte model needs (host side, from the generated batch)."""
+    keys = bt["keys"]
+    off = bt["offsets"]
+    F = w.n_fields
+    bag = np.repeat(np.arange(off.size - 1, dtype=np.int64), np.diff(off.astype(np.int64)))
+    width = dims[bag % F].astype(np.int64)           # row width of each occurrence
+    u, inv, cnt = np.unique(keys, return_inverse=True, return_counts=True)
+    uw = np.zeros(u.size, dtype=np.int64)
+    uw[inv] = width
+    long_u = cnt > LONG_SEGMENT
+    occ_long = long_u[inv]
+    return {
+        "nnz": int(keys.size), "U": int(u.size), "bags": int(off.size - 1),
+        "occ_elems": int(width.sum()),                      # sum of D over occurrences
+        "bag_elems": int(dims.sum()) * (off.size - 1) // F,  # sum of D over bags
+        "u_elems_short": int(uw[~long_u].sum()), "u_elems_long": int(uw[long_u].sum()),
+        "occ_short": int((~occ_long).sum()), "occ_long": int(occ_long.sum()),
+        "occ_elems_short": int(width[~occ_long].sum()), "occ_elems_long": int(width[occ_long].sum()),
+        "u_long": int(long_u.sum()),
+    }
+
+
+def kernel_bytes(name, st, w, passes):
+    """Algorithmic bytes one launch of `name` moves for a batch with stats `st`: every datum the
+    kernel must read or write once (no cache reuse), as in the design's byte model."""
+    sr = 2 if w.row_dtype == "f16" else 4
+    so = 2 if w.out_dtype == "f16" else 4
+    sg = 2 if w.grad_dtype == "f16" else 4
+    m = 1 if w.has_master else 0
+    state = 2 * sr + 8 + 8 * m                          # per element: row r/w, acc r/w, master r/w
+    n = st["nnz"]
+    if name == "lookup_pool":
+        # key in, slot hit (key compare + row prefix), row gather, rowref out; offsets, pooled out
+        return n * (8 + 12 + 4) + st["occ_elems"] * sr + st["bags"] * 4 + st["bag_elems"] * so
+    if name == "sort_hist":
+        return n * 4
+    if name == "sort_scan":
+        tiles = (n + 2047) // 2048
+        return 256 * tiles * 8
+    if name == "sort_scatter":
+        return n * 16 / 1.0
+    if name == "update_short":
+        return st["occ_short"] * 8 + st["occ_elems_short"] * sg + st["u_elems_short"] * state
+    if name == "update_long":
+        return st["occ_long"] * 8 + st["occ_elems_long"] * sg + st["u_elems_long"] * state
+    return 0
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch from rocprofv3 counters, if measured on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+        e = t[workload][kernel]
+        if e.get("src_hash") != kernel_src_hash():
+            return None
+        return float(e["bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline_child(name: str, max_seconds: float):
+    """Time the oracle's forward + backward on batch 0 of the workload (one thread)."""
+    from gen import synth, workloads as W
+    from oracle import emb_oracle as O
+    w = W.get(name)
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    dims = synth.field_dims(w)
+    t0 = time.perf_counter()
+    ot = O.Table(keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor, w.acc_init, rows,
+                 master=master)
+    build_s = time.perf_counter() - t0
+    bt = synth.batch(w, 0)
+    t0 = time.perf_counter()
+    ot.forward(bt["keys"], bt["offsets"], w.out_dtype)
+    t_fwd = time.perf_counter() - t0
+    u, _, _, _ = ot.backward(bt["keys"], bt["offsets"], bt["grad"], w.lr, w.eps)
+    t = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    print(json.dumps({"seconds": t, "fwd_seconds": t_fwd, "build_seconds": build_s,
+                      "nnz": int(bt["keys"].size), "U": int(u.size), "cpu": cpu,
+                      "nproc": os.cpu_count()}))
+
+
+def run_cpu_baseline(name: str):
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    code = ("import os,sys; os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]}); "
+            f"sys.path.insert(0, {ROOT!r}); import bench; bench.cpu_baseline_child({name!r}, 60)")
+    r = subprocess.run([sys.executable, "-c", code], env=env, stdout=subprocess.PIPE,
+                       stderr=subprocess.PIPE, text=True, timeout=900)
+    if r.returncode != 0:
+        log(r.stderr[-2000:])
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="f26")
+    ap.add_argument("--ring", type=int, default=0, help="distinct batches cycled (0 = workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        sys.exit("bench.py measures one GPU: this build has no multi-GPU path (the sharded design "
+                 "is described, not built); run with --gpus 1")
+
+    import torch
+    from ad_recommendation_amd import emb
+    from gen import synth, workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = W.get(args.workload)
+    R = args.ring or min(w.ring, 16)
+    dims = synth.field_dims(w)
+    t0 = time.perf_counter()
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    log(f"[bench] {w.name}: {keys.size} keys generated in {time.perf_counter() - t0:.1f}s")
+    t0 = time.perf_counter()
+    T = emb.Table(dims, emb.EMB_F16 if w.row_dtype == "f16" else emb.EMB_F32, w.has_master,
+                  w.n_tables, w.load_factor, w.acc_init, keys, rows, None, master)
+    del rows, master
+    log(f"[bench] table built in {time.perf_counter() - t0:.1f}s; arena "
+        f"{T.info['arena_bytes'] / 2**30:.2f} GiB")
+    T.flash(dev)
+    torch.cuda.synchronize()
+
+    odt = torch.float16 if w.out_dtype == "f16" else torch.float32
+    out_code = emb.EMB_F16 if w.out_dtype == "f16" else emb.EMB_F32
+    g_code = emb.EMB_F16 if w.grad_dtype == "f16" else emb.EMB_F32
+    ring = []
+    ws_bytes = 0
+    for b in range(R):
+        bt = synth.batch(w, b)
+        st = batch_stats(w, bt, dims)
+        n_bags = bt["offsets"].size - 1
+        ring.append({
+            "keys": torch.from_numpy(bt["keys"]).to(dev),
+            "offsets": torch.from_numpy(bt["offsets"]).to(dev),
+            "grad": torch.from_numpy(bt["grad"]).to(dev),
+            "out": torch.empty(w.batch, int(dims.sum()), dtype=odt, device=dev),
+            "rowref": torch.empty(max(1, st["nnz"]), dtype=torch.int32, device=dev),
+            "n_bags": n_bags, "nnz": st["nnz"], "st": st,
+        })
+        ws_bytes = max(ws_bytes, emb.bwd_workspace_bytes(T.h, n_bags, st["nnz"]))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    n_unique = torch.zeros(R, dtype=torch.int64, device=dev)
+    passes = 0
+    while passes < 4 and (T.info["rowref_space"] >> (8 * passes)) > 0:
+        passes += 1
+    log(f"[bench] ring of {R} batches staged; mean nnz {np.mean([r['nnz'] for r in ring]):.0f}, "
+        f"mean unique {np.mean([r['st']['U'] for r in ring]):.0f}")
+
+    def step(i):
+        r = ring[i % R]
+        emb.lookup_pool_fwd(T.h, r["keys"], r["offsets"], r["n_bags"], r["nnz"], r["out"],
+                            out_code, r["rowref"])
+        emb.sparse_adagrad_bwd(T.h, r["rowref"], r["offsets"], r["n_bags"], r["nnz"], r["grad"],
+                               g_code, w.lr, w.eps, ws, n_unique=n_unique[i % R:i % R + 1])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # calibration: every kernel timed over one pass of the ring
+    emb.emb_timing_enable(T.h, True)
+    for i in range(R):
+        step(i)
+    torch.cuda.synchronize()
+    calib = emb.emb_timing_read(T.h)
+    per_step = {k: v[1] / R for k, v in calib.items()}
+    dominant = max(per_step, key=per_step.get)
+    log("[bench] per-step kernel time (ms): " +
+        ", ".join(f"{k} {v:.4f}" for k, v in sorted(per_step.items(), key=lambda x: -x[1])))
+    got_u = n_unique.cpu().numpy()
+    want_u = np.array([r["st"]["U"] for r in ring])
+    if not np.array_equal(got_u, want_u):
+        sys.exit(f"unique-row counts differ from the batches' distinct keys: {got_u} vs {want_u}")
+
+    # timed region: K steps, only the dominant kernel bracketed by events
+    emb.emb_timing_enable(T.h, True, dominant)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    dom = emb.emb_timing_read(T.h)[dominant]
+    emb.emb_timing_enable(T.h, False)
+
+    rows_done = sum(ring[i % R]["nnz"] + ring[i % R]["st"]["U"] for i in range(args.steps))
+    value = rows_done / (ms / 1e3)
+    # algorithmic bytes of the dominant kernel over its timed launches
+    per_step_launches = dom[0] / args.steps
+    dom_bytes = sum(kernel_bytes(dominant, ring[i % R]["st"], w, passes) for i in range(args.steps))
+    dom_bytes *= per_step_launches
+    achieved = dom_bytes / (dom[1] / 1e3) / 1e9
+    traffic = load_traffic(w.name, dominant)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        c = run_cpu_baseline(w.name) if w.n_keys <= 50_000_000 else None
+        if c:
+            cpu = {"value": (c["nnz"] + c["U"]) / c["seconds"], "unit": "rows/s", "cores": 1,
+                   "kind": "oracle",
+                   "sample": f"one full batch (batch 0: {c['nnz']} lookups, {c['U']} rows updated) "
+                             f"of {w.name}, oracle forward+backward, 1 thread on {c['cpu']} "
+                             f"({c['nproc']} cpus visible); table build {c['build_seconds']:.1f}s "
+                             f"excluded; {c['seconds']:.2f}s"}
+    res = {
+        "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.row_dtype == "f32" else "f16 rows/f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": w.name, "fields": w.n_fields, "resident_keys": w.n_keys,
+                   "dim": w.dim if w.dim else "per-field", "row_dtype": w.row_dtype,
+                   "master": w.has_master, "tables": w.n_tables, "batch": w.batch,
+                   "ring": R, "mean_lookups_per_step": float(np.mean([r["nnz"] for r in ring])),
+                   "mean_rows_updated_per_step": float(np.mean([r["st"]["U"] for r in ring])),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "avg_launch_ms": dom[1] / max(dom[0], 1),
+                     "alg_bytes_per_launch": dom_bytes / max(dom[0], 1)},
+        "cpu_baseline": cpu,
+        "kernel_ms_per_step": per_step,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
