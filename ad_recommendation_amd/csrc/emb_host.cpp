@@ -545,6 +545,8 @@ int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets
   if (n_bags > 0 && (!d_offsets || !d_out)) return fail(EMB_EINVAL, "null offsets or output");
   if (nnz > 0 && n_bags == 0) return fail(EMB_EINVAL, "occurrences without bags");
   if (nnz > 0 && (!d_keys || !d_rowref)) return fail(EMB_EINVAL, "null keys or rowref");
+  if ((reinterpret_cast<uintptr_t>(d_out) | reinterpret_cast<uintptr_t>(d_rowref)) % 16)
+    return fail(EMB_EINVAL, "d_out and d_rowref must be 16-byte aligned");
   if (!t->flashed) return fail(EMB_ESTATE, "lookup before pass_flash");
   FwdLaunch a{};
   a.d = t->dev();
@@ -566,7 +568,7 @@ int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets
 int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* bytes) {
   if (!t || !bytes) return fail(EMB_EINVAL, "null argument");
   if (n_bags < 0 || nnz < 0 || nnz >= (1ll << 31)) return fail(EMB_EINVAL, "bad sizes");
-  *bytes = plan_bwd(nnz, t->rowref_space).bytes;
+  *bytes = plan_bwd(nnz, t->rowref_space, t->max_dim, t->row_dtype == EMB_F16).bytes;
   return EMB_OK;
 }
 
@@ -583,7 +585,10 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
   if (nnz > 0 && (!d_rowref || !d_offsets || !d_grad || !d_ws))
     return fail(EMB_EINVAL, "null rowref, offsets, grad or workspace");
   if (d_count && !d_unique) return fail(EMB_EINVAL, "d_count needs d_unique");
-  const BwdPlan p = plan_bwd(nnz, t->rowref_space);
+  if ((reinterpret_cast<uintptr_t>(d_grad) | reinterpret_cast<uintptr_t>(d_rowref) |
+       reinterpret_cast<uintptr_t>(d_ws)) % 16)
+    return fail(EMB_EINVAL, "d_grad, d_rowref and d_ws must be 16-byte aligned");
+  const BwdPlan p = plan_bwd(nnz, t->rowref_space, t->max_dim, t->row_dtype == EMB_F16);
   if (nnz > 0 && ws_bytes < p.bytes) return fail(EMB_ENOSPACE, "workspace smaller than bwd_workspace_bytes()");
   if (!t->flashed) return fail(EMB_ESTATE, "backward before pass_flash");
   BwdLaunch a{};

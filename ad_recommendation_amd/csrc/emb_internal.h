@@ -114,13 +114,19 @@ struct BwdLaunch {
 // Workspace carve-up for the backward (same on host and device side).
 struct BwdPlan {
   int32_t n;           // items (occurrences)
+  int32_t ipt;         // sort items per thread (tile = 256 * ipt)
   int32_t tiles;       // sort tiles
-  int32_t passes;      // 8-bit radix passes
-  uint32_t miss_key;   // key given to missed occurrences (sorts last)
-  size_t off_ka, off_va, off_kb, off_vb, off_counts, off_tot, off_ctr, off_long, off_seg;
+  int32_t passes;      // radix passes
+  int32_t bits;        // digit bits per pass (<= 11); one extra bin holds misses
+  int32_t gsl;         // log2 lanes per row in the update kernels
+  int32_t rounds;      // rounds per update piece
+  int32_t n_pieces;    // update pieces
+  int32_t pdim;        // floats per partial
+  size_t off_ka, off_va, off_kb, off_vb, off_counts, off_tot, off_ctr, off_seg;
+  size_t off_phead, off_ptail, off_pflag, off_pkey;
   size_t bytes;
 };
-BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space);
+BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t row_f16);
 
 // Launchers (emb_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx);

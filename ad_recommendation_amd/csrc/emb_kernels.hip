@@ -140,8 +140,8 @@ __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, in
 }
 
 // ---------------------------------------------------------------- forward: probe + sum pool
-constexpr int kFwdBags = 256;    // bags per block
-constexpr int kFwdKeyCap = 4096; // rowrefs staged in LDS; larger blocks re-read them from HBM/L2
+constexpr int kFwdBags = 64;     // bags per block
+constexpr int kFwdKeyCap = 2048; // rowrefs staged in LDS; larger blocks re-read them from HBM/L2
 
 template <typename RowT, typename OutT>
 __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2) {
@@ -221,11 +221,12 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
 }
 
 // ---------------------------------------------------------------- backward: radix sort
-constexpr int kIPT = 8;                       // items per thread per sort tile
-constexpr int kTile = kBlock * kIPT;          // 2048
+// Stable LSD radix sort of (rowref, bag) pairs.  Digits are up to 11 bits wide, chosen so the row
+// space needs as few passes as possible; occurrences that missed get a bin of their own after
+// every digit value, so they never widen the key and always sort last.
 constexpr int kOffStage = 2048;               // bag offsets staged in LDS for the first pass
-constexpr int kQ = 16;                        // sorted items scanned per lane group (update pass)
-constexpr int kLong = 32;                     // segments longer than this take the block path
+constexpr int kMaxBins = (1 << 11) + 1;
+constexpr uint32_t kMissKey = 0xFFFFFFFFu;    // sorted-key value of a missed occurrence
 
 struct SortArgs {
   const uint32_t* rowref;   // first pass source
@@ -235,51 +236,108 @@ struct SortArgs {
   const uint32_t* vin;
   uint32_t* kout;
   uint32_t* vout;
-  uint32_t* counts;   // [256][tiles]
-  uint32_t* tot;      // [256]
+  uint32_t* counts;   // [bins][tiles]
+  uint32_t* tot;      // [bins]
   uint32_t* ctr;      // small counters, zeroed by the first scan
   int32_t n;
   int32_t tiles;
-  uint32_t miss_key;
+  int32_t tile;       // items per tile
+  uint32_t rowref_space;
   int32_t shift;
+  int32_t bits;       // digit bits of this pass; bin (1 << bits) holds the misses
 };
 
-// Sort key of an occurrence: its rowref, or miss_key (= rowref space, sorts last) for a miss or any
-// value outside the table.
-__device__ __forceinline__ uint32_t first_key(uint32_t rr, uint32_t miss_key) {
-  return rr >= miss_key ? miss_key : rr;
+__device__ __forceinline__ uint32_t sort_key_of(uint32_t rr, uint32_t space) {
+  return rr < space ? rr : kMissKey;  // a miss, or any value outside the table
+}
+__device__ __forceinline__ uint32_t digit_of(uint32_t k, int shift, int bits) {
+  return k == kMissKey ? (1u << bits) : ((k >> shift) & ((1u << bits) - 1u));
 }
 
-// Per-tile histogram of one 8-bit digit.
+// Exclusive scan of n <= 256*E values get(i) into set(i, prefix) by one block; returns the total.
+template <int E, typename Get, typename Set>
+__device__ __forceinline__ uint32_t block_scan_n(int n, Get get, Set set, uint32_t* s_w) {
+  const int b = threadIdx.x * E;
+  uint32_t v[E], sum = 0;
+#pragma unroll
+  for (int u = 0; u < E; ++u) {
+    v[u] = (b + u < n) ? get(b + u) : 0u;
+    sum += v[u];
+  }
+  uint32_t total;
+  uint32_t pre = block_excl_scan(sum, s_w, total);
+#pragma unroll
+  for (int u = 0; u < E; ++u) {
+    if (b + u < n) set(b + u, pre);
+    pre += v[u];
+  }
+  return total;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  This maps block b
+// to a logical index so that every XCD works on one contiguous range of [0, n): neighbouring
+// tiles (or bins) then share cache lines in one L2.
+__device__ __forceinline__ int xcd_index(int b, int n) {
+  const int q = n >> 3, r = n & 7, x = b & 7, j = b >> 3;
+  return x * q + min(x, r) + j;
+}
+
+// Per-tile histogram of one digit.  Each thread counts a run of consecutive items and adds runs
+// of equal digits at once (sorted passes hold long runs of one key).  counts is [tile][bin].
 template <bool FIRST>
 __global__ __launch_bounds__(kBlock) void k_sort_hist(SortArgs a) {
-  __shared__ uint32_t h[256];
-  const int t = blockIdx.x;
-  h[threadIdx.x] = 0;
+  __shared__ uint32_t h[kMaxBins];
+  const int t = xcd_index(blockIdx.x, a.tiles);
+  const int bins = (1 << a.bits) + 1;
+  for (int d = threadIdx.x; d < bins; d += kBlock) h[d] = 0;
   __syncthreads();
-  const int32_t i0 = t * kTile;
-  const int32_t i1 = min(a.n, i0 + kTile);
-  for (int32_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
-    const uint32_t k = FIRST ? first_key(a.rowref[i], a.miss_key) : a.kin[i];
-    atomicAdd(&h[(k >> a.shift) & 255u], 1u);
+  const int per = a.tile / kBlock;  // a multiple of 4
+  const int32_t i0 = t * a.tile + (int32_t)threadIdx.x * per;
+  const uint32_t* src = FIRST ? a.rowref : a.kin;
+  uint32_t prev = 0xFFFFFFFFu, run = 0;
+  for (int u = 0; u < per; u += 4) {
+    const int32_t i = i0 + u;
+    uint32_t k4[4];
+    if (i + 3 < a.n) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + i);
+      k4[0] = v.x; k4[1] = v.y; k4[2] = v.z; k4[3] = v.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) k4[q] = i + q < a.n ? src[i + q] : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (i + q >= a.n) break;
+      const uint32_t k = FIRST ? sort_key_of(k4[q], a.rowref_space) : k4[q];
+      const uint32_t dg = digit_of(k, a.shift, a.bits);
+      if (dg != prev) {
+        if (run) atomicAdd(&h[prev], run);
+        prev = dg;
+        run = 0;
+      }
+      ++run;
+    }
   }
+  if (run) atomicAdd(&h[prev], run);
   __syncthreads();
-  a.counts[(size_t)threadIdx.x * a.tiles + t] = h[threadIdx.x];
+  for (int d = threadIdx.x; d < bins; d += kBlock) a.counts[(size_t)t * bins + d] = h[d];
 }
 
-// Exclusive scan of each digit's per-tile counts (one block per digit) and the digit totals.
+// Exclusive scan of each digit's per-tile counts (one block per digit, reading a column of the
+// [tile][bin] matrix; neighbouring digits run on one XCD so they share lines) and digit totals.
 __global__ __launch_bounds__(kBlock) void k_sort_scan(SortArgs a, int zero_ctr) {
   __shared__ uint32_t s_w[kWaves];
-  const int d = blockIdx.x;
-  if (zero_ctr && d == 0 && threadIdx.x < 16) a.ctr[threadIdx.x] = 0;
-  uint32_t* row = a.counts + (size_t)d * a.tiles;
+  const int bins = (1 << a.bits) + 1;
+  const int d = xcd_index(blockIdx.x, bins);
+  if (zero_ctr && blockIdx.x == 0 && threadIdx.x < 16) a.ctr[threadIdx.x] = 0;
+  uint32_t* col = a.counts + d;
   uint32_t carry = 0;
   for (int32_t c0 = 0; c0 < a.tiles; c0 += kBlock * 4) {
     uint32_t v[4], s = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int32_t i = c0 + threadIdx.x * 4 + u;
-      v[u] = i < a.tiles ? row[i] : 0u;
+      v[u] = i < a.tiles ? col[(size_t)i * bins] : 0u;
       s += v[u];
     }
     uint32_t total;
@@ -287,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void k_sort_scan(SortArgs a, int zero_ctr) 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int32_t i = c0 + threadIdx.x * 4 + u;
-      if (i < a.tiles) row[i] = pre;
+      if (i < a.tiles) col[(size_t)i * bins] = pre;
       pre += v[u];
     }
     carry += total;
@@ -305,74 +363,93 @@ __device__ __forceinline__ int32_t bag_search_global(const int32_t* off, int32_t
   return lo;
 }
 
-// Stable scatter of one tile by one 8-bit digit.  Each wave ranks a contiguous quarter of the
-// tile with ballots, the tile is reordered in LDS, then written out in digit runs.
-template <bool FIRST>
+// Last bag j in [0, n_bags) with off[j] <= pos, found by the whole block: each round probes 256
+// evenly spaced offsets and keeps the bracket containing pos (off is non-decreasing).
+__device__ int32_t block_find_bag(const int32_t* off, int32_t n_bags, int32_t pos) {
+  int32_t lo = 0, hi = n_bags - 1;
+  while (hi - lo >= kBlock) {
+    const int32_t step = (hi - lo) / kBlock + 1;
+    const int32_t p = lo + (int32_t)threadIdx.x * step;
+    const int c = __syncthreads_count(p <= hi && off[p] <= pos);
+    const int32_t nlo = lo + (c > 0 ? c - 1 : 0) * step;
+    hi = min(hi, nlo + step - 1);
+    lo = nlo;
+  }
+  const int32_t p = lo + (int32_t)threadIdx.x;
+  const int c = __syncthreads_count(p <= hi && off[p] <= pos);
+  return lo + (c > 0 ? c - 1 : 0);
+}
+
+// Stable scatter of one tile by one digit.  Each wave ranks a contiguous quarter of the tile with
+// ballots (one per digit bit, plus the miss bin), the tile is reordered in LDS, then written out
+// in digit runs.  IPT items per thread; digits of at most LOGB bits.
+template <bool FIRST, int IPT, int LOGB>
 __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
-  __shared__ uint32_t s_key[kTile];
-  __shared__ uint32_t s_val[kTile];
-  __shared__ uint32_t s_wcnt[kWaves][256];
-  __shared__ uint32_t s_gbase[256];
-  __shared__ uint32_t s_lstart[256];
+  constexpr int TILE = kBlock * IPT;
+  constexpr int BINS = (1 << LOGB) + 1;
+  constexpr int E = (BINS + kBlock - 1) / kBlock;
+  __shared__ uint32_t s_key[TILE];
+  __shared__ uint32_t s_val[TILE];
+  __shared__ uint32_t s_wcnt[kWaves][BINS];
+  __shared__ uint32_t s_gbase[BINS];
+  __shared__ uint32_t s_lstart[BINS];
   __shared__ uint32_t s_w[kWaves];
   __shared__ int32_t s_off[FIRST ? kOffStage + 1 : 1];
-  __shared__ int32_t s_jlo, s_jhi;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
-  const int t = blockIdx.x;
-  const int32_t i0 = t * kTile;
-  const int32_t tn = min(kTile, a.n - i0);
+  const int t = xcd_index(blockIdx.x, a.tiles);
+  const int32_t i0 = t * TILE;
+  const int32_t tn = min(TILE, a.n - i0);
+  const int bins = (1 << a.bits) + 1;
 
-  // global start of each digit: digits below it over all tiles, plus this digit in earlier tiles
-  {
-    uint32_t total;
-    const uint32_t below = block_excl_scan(a.tot[tid], s_w, total);
-    s_gbase[tid] = below + a.counts[(size_t)tid * a.tiles + t];
-    for (int ww = 0; ww < kWaves; ++ww) s_wcnt[ww][tid] = 0;
-  }
+  // global start of each digit in this tile: all smaller digits, plus this digit in earlier tiles
+  block_scan_n<E>(bins, [&](int d) { return a.tot[d]; },
+                  [&](int d, uint32_t v) { s_gbase[d] = v + a.counts[(size_t)t * bins + d]; },
+                  s_w);
+  for (int d = tid; d < bins; d += kBlock)
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) s_wcnt[ww][d] = 0;
   bool stage = false;
+  int32_t jlo = 0, nst = 0;
   if (FIRST) {
-    if (tid == 0) {
-      s_jlo = bag_search_global(a.offsets, 0, a.n_bags - 1, i0);
-      s_jhi = bag_search_global(a.offsets, 0, a.n_bags - 1, i0 + tn - 1);
-    }
+    // bags of this tile's occurrences: stage offsets[jlo ..] in LDS when they cover the tile
+    jlo = block_find_bag(a.offsets, a.n_bags, i0);
+    nst = min(kOffStage + 1, a.n_bags - jlo + 1);
+    for (int i = tid; i < nst; i += kBlock) s_off[i] = a.offsets[jlo + i];
     __syncthreads();
-    stage = (s_jhi - s_jlo + 2) <= kOffStage + 1;
-    if (stage)
-      for (int i = tid; i <= s_jhi - s_jlo + 1; i += kBlock) s_off[i] = a.offsets[s_jlo + i];
+    stage = (jlo + nst - 1 == a.n_bags) || (s_off[nst - 1] > i0 + tn - 1);
   }
   __syncthreads();
 
-  uint32_t key[kIPT], val[kIPT], rank[kIPT];
+  uint32_t key[IPT], val[IPT], rank[IPT];
   const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int k = 0; k < kIPT; ++k) {
-    const int32_t li = w * (kIPT * 64) + k * 64 + lane;  // item index inside the tile
+  for (int k = 0; k < IPT; ++k) {
+    const int32_t li = w * (IPT * 64) + k * 64 + lane;  // item index inside the tile
     const bool valid = li < tn;
     const int32_t i = i0 + li;
     uint32_t kk = 0, vv = 0;
     if (valid) {
       if (FIRST) {
-        kk = first_key(a.rowref[i], a.miss_key);
+        kk = sort_key_of(a.rowref[i], a.rowref_space);
         if (stage) {
-          int lo = 0, hi = s_jhi - s_jlo;
+          int lo = 0, hi = nst - 2;
           while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_off[mid] <= i) lo = mid; else hi = mid - 1;
           }
-          vv = (uint32_t)(s_jlo + lo);
+          vv = (uint32_t)(jlo + lo);
         } else {
-          vv = (uint32_t)bag_search_global(a.offsets, s_jlo, s_jhi, i);
+          vv = (uint32_t)bag_search_global(a.offsets, jlo, a.n_bags - 1, i);
         }
       } else {
         kk = a.kin[i];
         vv = a.vin[i];
       }
     }
-    const uint32_t dg = (kk >> a.shift) & 255u;
+    const uint32_t dg = digit_of(kk, a.shift, a.bits);
     uint64_t m = __ballot(valid);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
+    for (int bit = 0; bit <= a.bits; ++bit) {
       const uint64_t bb = __ballot((dg >> bit) & 1u);
       m &= ((dg >> bit) & 1u) ? bb : ~bb;
     }
@@ -383,23 +460,26 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
     val[k] = vv;
   }
   __syncthreads();
-  // per digit: counts in earlier waves and the tile-local start
-  {
+  // per digit: items in earlier waves, and the digit's start inside the reordered tile
+  for (int d = tid; d < bins; d += kBlock) {
     uint32_t c = 0;
+#pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const uint32_t x = s_wcnt[ww][tid];
-      s_wcnt[ww][tid] = c;
+      const uint32_t x = s_wcnt[ww][d];
+      s_wcnt[ww][d] = c;
       c += x;
     }
-    uint32_t total;
-    s_lstart[tid] = block_excl_scan(c, s_w, total);
+    s_lstart[d] = c;  // per-digit tile count, scanned below
   }
   __syncthreads();
+  block_scan_n<E>(bins, [&](int d) { return s_lstart[d]; },
+                  [&](int d, uint32_t v) { s_lstart[d] = v; }, s_w);
+  __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kIPT; ++k) {
-    const int32_t li = w * (kIPT * 64) + k * 64 + lane;
+  for (int k = 0; k < IPT; ++k) {
+    const int32_t li = w * (IPT * 64) + k * 64 + lane;
     if (li < tn) {
-      const uint32_t dg = (key[k] >> a.shift) & 255u;
+      const uint32_t dg = digit_of(key[k], a.shift, a.bits);
       const uint32_t p = s_lstart[dg] + s_wcnt[w][dg] + rank[k];
       s_key[p] = key[k];
       s_val[p] = val[k];
@@ -408,7 +488,7 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
   __syncthreads();
   for (int p = tid; p < tn; p += kBlock) {
     const uint32_t kk = s_key[p];
-    const uint32_t dg = (kk >> a.shift) & 255u;
+    const uint32_t dg = digit_of(kk, a.shift, a.bits);
     const uint32_t dst = s_gbase[dg] + ((uint32_t)p - s_lstart[dg]);
     a.kout[dst] = kk;
     a.vout[dst] = s_val[p];
@@ -418,162 +498,261 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
 // ---------------------------------------------------------------- backward: reduce + Adagrad
 struct UpdArgs {
   DevDesc d;
-  const uint32_t* key;   // sorted rowrefs (miss_key last)
+  const uint32_t* key;   // sorted rowrefs (misses last, as kMissKey)
   const uint32_t* val;   // bag of each sorted occurrence
   int32_t n;
   uint32_t miss_key;
   const void* grad;
   float lr, eps;
-  uint32_t* ctr;         // [0] long-segment count, [1] unique count
-  uint32_t* long_list;
+  uint32_t* ctr;         // [1] unique-row count
   int64_t* n_unique;
+  // pieces: each wave reduces `rounds` x (64 / GS) consecutive sorted occurrences
+  int32_t rounds;
+  int32_t n_pieces;
+  int32_t pdim;          // floats per partial (widest row)
+  float* phead;          // [n_pieces][pdim] sum of the piece's first segment when it began earlier
+  float* ptail;          // [n_pieces][pdim] sum of the piece's last segment when it runs on
+  uint32_t* pflag;       // [n_pieces] bit 0: tail partial; bits 1-2: head partial (1 ends here, 2 passes)
+  uint32_t* pkey;        // [n_pieces][2] row and width of the tail partial's segment
 };
+
+// Row state of one lane's EPL elements, read ahead of the update.
+template <int EPL>
+struct RowState {
+  typename F32V<EPL>::t acc, w;
+};
+
+template <typename RowT, int EPL>
+__device__ __forceinline__ RowState<EPL> load_state(const UpdArgs& a, uint32_t r, int e0) {
+  RowState<EPL> st;
+  const uint64_t e = (uint64_t)r * a.d.granule + e0;
+  st.acc = load_f32<float, EPL>(a.d.acc + e);
+  if (sizeof(RowT) == 2 && a.d.has_master) st.w = load_f32<float, EPL>(a.d.master + e);
+  else st.w = load_f32<RowT, EPL>(reinterpret_cast<const RowT*>(a.d.rows) + e);
+  return st;
+}
+
+// Element-wise Adagrad on one lane's elements: acc += g^2; w -= lr * g / (sqrt(acc) + eps).
+// fp16 rows with a master copy update the master and store its fp16 rounding as the row.
+template <typename RowT, int EPL>
+__device__ __forceinline__ void apply_state(const UpdArgs& a, uint32_t r, int e0,
+                                            typename F32V<EPL>::t g, RowState<EPL> st) {
+  typedef typename F32V<EPL>::t V;
+  const uint64_t e = (uint64_t)r * a.d.granule + e0;
+  const V acc = st.acc + g * g;
+  V den;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) den[q] = __builtin_sqrtf(acc[q]) + a.eps;
+  const V w = st.w - (a.lr * g) / den;
+  store_from_f32<float, EPL>(a.d.acc + e, acc);
+  RowT* rows = reinterpret_cast<RowT*>(a.d.rows);
+  if (sizeof(RowT) == 2 && a.d.has_master) store_from_f32<float, EPL>(a.d.master + e, w);
+  store_from_f32<RowT, EPL>(rows + e, w);
+}
 
 template <typename RowT, int EPL>
 __device__ __forceinline__ void adagrad_row(const UpdArgs& a, uint32_t r, int e0,
                                             typename F32V<EPL>::t g) {
-  typedef typename F32V<EPL>::t V;
-  const uint64_t e = (uint64_t)r * a.d.granule + e0;
-  V acc = load_f32<float, EPL>(a.d.acc + e);
-  acc += g * g;
-  V den;
-#pragma unroll
-  for (int q = 0; q < EPL; ++q) den[q] = __builtin_sqrtf(acc[q]) + a.eps;
-  const V delta = (a.lr * g) / den;
-  store_from_f32<float, EPL>(a.d.acc + e, acc);
-  RowT* rows = reinterpret_cast<RowT*>(a.d.rows);
-  if constexpr (sizeof(RowT) == 4) {
-    V w = load_f32<RowT, EPL>(rows + e);
-    store_from_f32<RowT, EPL>(rows + e, w - delta);
-  } else if (a.d.has_master) {
-    V m = load_f32<float, EPL>(a.d.master + e) - delta;
-    store_from_f32<float, EPL>(a.d.master + e, m);
-    store_from_f32<RowT, EPL>(rows + e, m);
-  } else {
-    V w = load_f32<RowT, EPL>(rows + e);
-    store_from_f32<RowT, EPL>(rows + e, w - delta);
-  }
+  apply_state<RowT, EPL>(a, r, e0, g, load_state<RowT, EPL>(a, r, e0));
 }
 
-// Each group of 2^gs_log2 lanes owns kQ consecutive sorted occurrences and every segment that
-// starts among them.  Segments of at most kLong occurrences are reduced and updated here; longer
-// ones are queued for k_update_long.
-template <typename RowT, typename GradT>
-__global__ __launch_bounds__(kBlock) void k_update_short(UpdArgs a, int gs_log2) {
-  constexpr int EPL = 16 / (int)sizeof(RowT);
+template <typename GradT, int EPL>
+__device__ __forceinline__ typename F32V<EPL>::t grad_slice(const UpdArgs& a, uint32_t bag,
+                                                            int e0, int& D) {
   typedef typename F32V<EPL>::t V;
-  __shared__ uint32_t s_cnt;
-  if (threadIdx.x == 0) s_cnt = 0;
-  __syncthreads();
-  const int lane = threadIdx.x & ((1 << gs_log2) - 1);
-  const int64_t grp = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> gs_log2;
-  const int64_t c0 = grp * kQ;
-  const GradT* G = reinterpret_cast<const GradT*>(a.grad);
   const int F = a.d.n_fields;
-  const int e0 = lane * EPL;
+  const int f = (int)(bag % (uint32_t)F);
+  D = a.d.var_dim ? a.d.fdim[f] : a.d.fixed_dim;
+  if (e0 >= D) return V(0.0f);
+  const int col = a.d.var_dim ? a.d.fcol[f] : f * a.d.fixed_dim;
+  const GradT* G = reinterpret_cast<const GradT*>(a.grad);
+  return load_f32<GradT, EPL>(G + (uint64_t)(bag / (uint32_t)F) * a.d.out_width + col + e0);
+}
+
+// Segmented inclusive scan of one round across the wave's lane groups.  Segments are runs of
+// equal keys, so key equality marks them; the carry adds the part of the first segment that lies
+// in earlier rounds.  Returns the segment sum so far; updates the carry (the last group's sum,
+// its key, and the index of its segment's first occurrence).
+template <int EPL>
+__device__ __forceinline__ typename F32V<EPL>::t seg_scan(int gs_log2, int64_t i, uint32_t kr,
+                                                          typename F32V<EPL>::t xr,
+                                                          uint32_t& carry_key,
+                                                          typename F32V<EPL>::t& carry,
+                                                          int64_t& carry_head) {
+  typedef typename F32V<EPL>::t V;
+  const int GS = 1 << gs_log2;
+  const int IPR = 64 >> gs_log2;
+  const int lane = lane_id();
+  const int li = lane & (GS - 1);
+  const int g = lane >> gs_log2;
+  for (int d = 1; d < IPR; d <<= 1) {
+    V y;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) y[q] = __shfl_up(xr[q], d * GS, 64);
+    const uint32_t ky = __shfl_up(kr, d * GS, 64);
+    if (g >= d && ky == kr) xr += y;
+  }
+  if (kr == carry_key) xr += carry;
+  const int src = (IPR - 1) * GS + li;
+  V nc;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) nc[q] = __shfl(xr[q], src, 64);
+  const uint32_t nk = __shfl(kr, src, 64);
+  if (nk != carry_key) {
+    const uint64_t m = __ballot(kr == nk);
+    const int first = m ? (__builtin_ctzll(m) >> gs_log2) : 0;
+    carry_head = i - g + first;
+  }
+  carry = nc;
+  carry_key = nk;
+  return xr;
+}
+
+template <int EPL> struct SegBatch { static constexpr int value = EPL == 4 ? 4 : 2; };
+
+constexpr uint32_t kHeadEnds = 1u, kHeadPasses = 2u;
+
+// Segmented gradient reduction in sorted order fused with the Adagrad update.  Each wave owns
+// pieces of `rounds` x (64/GS) consecutive sorted occurrences (lane group g of a round holds one
+// occurrence).  A segmented scan across the groups, with a carry between rounds, sums each row's
+// occurrences in order.  A segment that begins and ends inside the piece is applied at its last
+// occurrence.  The piece's first segment, when it began in an earlier piece, is left as a head
+// partial; its last segment, when it runs into the next piece, as a tail partial; k_update_fixup
+// joins them.  Loads are issued a batch of rounds at a time: keys first, then gradient slices
+// together with the state of the rows that end in the batch.
+template <typename RowT, typename GradT>
+__global__ __launch_bounds__(kBlock) void k_update_pieces(UpdArgs a, int gs_log2) {
+  constexpr int EPL = 16 / (int)sizeof(RowT);
+  constexpr int BR = SegBatch<EPL>::value;
+  typedef typename F32V<EPL>::t V;
+  __shared__ uint32_t s_heads;
+  if (threadIdx.x == 0) s_heads = 0;
+  __syncthreads();
+  const int GS = 1 << gs_log2;
+  const int IPR = 64 >> gs_log2;
+  const int PW = a.rounds * IPR;
+  const int lane = lane_id();
+  const int li = lane & (GS - 1);
+  const int g = lane >> gs_log2;
+  const int e0 = li * EPL;
+  const uint32_t NONE = 0xFFFFFFFFu;  // above every row key; equal to the miss key
+  const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
   uint32_t heads = 0;
-  if (c0 < a.n) {
-    const int32_t c1 = (int32_t)min<int64_t>(a.n, c0 + kQ);
-    uint32_t prev = c0 > 0 ? a.key[c0 - 1] : 0xFFFFFFFFu;
-    for (int32_t i = (int32_t)c0; i < c1; ++i) {
-      const uint32_t k = a.key[i];
-      if (k == a.miss_key) break;
-      const bool head = (i == 0) || (k != prev);
-      prev = k;
-      if (!head) continue;
-      ++heads;
-      if (i + kLong < a.n && a.key[i + kLong] == k) {
-        if (lane == 0) a.long_list[atomicAdd(&a.ctr[0], 1u)] = (uint32_t)i;
-        continue;
+  for (int64_t c = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / 64; c < a.n_pieces; c += wstride) {
+    const int64_t p0 = c * PW;
+    const int64_t p1 = min((int64_t)a.n, p0 + PW);
+    const uint32_t k0 = a.key[p0];
+    // the piece's first segment began in an earlier piece
+    const bool cont = k0 < a.miss_key && p0 > 0 && a.key[p0 - 1] == k0;
+    uint32_t carry_key = NONE;
+    V carry = 0.0f;
+    int64_t carry_head = -1;
+    int carry_D = 0;
+    bool head_ended = false;
+    for (int rb = 0; rb < a.rounds; rb += BR) {
+      uint32_t k[BR], bag[BR];
+      bool own[BR], hd[BR], upd[BR], cend[BR];
+#pragma unroll
+      for (int r = 0; r < BR; ++r) {
+        const int64_t i = p0 + (int64_t)(rb + r) * IPR + g;
+        const bool valid = i < p1;
+        const uint32_t kk = valid ? a.key[i] : NONE;
+        const uint32_t kp = (valid && i > 0) ? a.key[i - 1] : NONE;
+        const uint32_t kn = (valid && i + 1 < a.n) ? a.key[i + 1] : NONE;
+        own[r] = kk < a.miss_key;
+        k[r] = own[r] ? kk : NONE;
+        hd[r] = own[r] && kp != kk;
+        const bool end = own[r] && kn != kk;
+        const bool is_cont = own[r] && cont && kk == k0;
+        upd[r] = end && !is_cont;
+        cend[r] = end && is_cont;
+        bag[r] = own[r] ? a.val[i] : 0u;
       }
-      const uint32_t bag0 = a.val[i];
-      const int f = (int)(bag0 % (uint32_t)F);
-      const int D = a.d.var_dim ? a.d.fdim[f] : a.d.fixed_dim;
-      if (e0 >= D) continue;
-      const int col = a.d.var_dim ? a.d.fcol[f] : f * a.d.fixed_dim;
-      const GradT* Gc = G + col + e0;
-      V g = 0.0f;
-      int32_t e = i;
-      for (;;) {
-        uint32_t bg[4];
-        bool ok[4];
+      V x[BR];
+      RowState<EPL> st[BR];
+      int D[BR];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ok[u] = (e + u < a.n) && (a.key[e + u] == k);
-          bg[u] = ok[u] ? a.val[e + u] : 0u;
-        }
-        V x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          x[u] = ok[u] ? load_f32<GradT, EPL>(Gc + (uint64_t)(bg[u] / (uint32_t)F) * a.d.out_width)
-                       : V(0.0f);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) g += x[u];
-        if (!ok[3]) break;
-        e += 4;
+      for (int r = 0; r < BR; ++r) {
+        D[r] = 0;
+        x[r] = own[r] ? grad_slice<GradT, EPL>(a, bag[r], e0, D[r]) : V(0.0f);
+        upd[r] = upd[r] && e0 < D[r];
+        if (upd[r]) st[r] = load_state<RowT, EPL>(a, k[r], e0);
       }
-      adagrad_row<RowT, EPL>(a, k, e0, g);
+#pragma unroll
+      for (int r = 0; r < BR; ++r) {
+        const int64_t i = p0 + (int64_t)(rb + r) * IPR + g;
+        const uint32_t prev_carry = carry_key;
+        const V sum = seg_scan<EPL>(gs_log2, i, k[r], x[r], carry_key, carry, carry_head);
+        if (carry_key != prev_carry) carry_D = __shfl(D[r], (IPR - 1) * GS, 64);
+        if (hd[r]) heads += (li == 0);
+        if (upd[r]) apply_state<RowT, EPL>(a, k[r], e0, sum, st[r]);
+        if (cend[r] && e0 < D[r]) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, sum);
+        head_ended = head_ended || (__ballot(cend[r]) != 0);
+      }
     }
+    // the last segment runs into the next piece: leave its sum for the fixup
+    uint32_t flag = head_ended ? (kHeadEnds << 1) : 0u;
+    if (carry_key < a.miss_key && p1 < a.n && a.key[p1] == carry_key) {
+      if (cont && carry_key == k0) {
+        flag |= kHeadPasses << 1;  // the first segment spans the whole piece
+        if (g == 0 && e0 < carry_D) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, carry);
+      } else {
+        flag |= 1u;
+        if (g == 0 && e0 < carry_D) store_from_f32<float, EPL>(a.ptail + c * a.pdim + e0, carry);
+        if (lane == 0) {
+          a.pkey[2 * c] = carry_key;
+          a.pkey[2 * c + 1] = (uint32_t)carry_D;
+        }
+      }
+    }
+    if (lane == 0) a.pflag[c] = flag;
   }
-  if (lane == 0 && heads) atomicAdd(&s_cnt, heads);
+  uint32_t wsum = 0;
+  for (int q = 0; q < 64; q += GS) wsum += __shfl(heads, q, 64);
+  if (lane == 0 && wsum) atomicAdd(&s_heads, wsum);
   __syncthreads();
-  if (threadIdx.x == 0 && s_cnt) atomicAdd(&a.ctr[1], s_cnt);
+  if (threadIdx.x == 0 && s_heads) atomicAdd(&a.ctr[1], s_heads);
 }
 
-// One block per long segment: every lane group strides through the segment, partial sums meet in
-// LDS, and one group applies the update.
-template <typename RowT, typename GradT>
-__global__ __launch_bounds__(kBlock) void k_update_long(UpdArgs a, int gs_log2) {
+// Joins the partial sums of segments that cross pieces.  One wave per piece with a tail partial:
+// it reads the flags of the following pieces 64 at a time to find where the segment ends, adds the
+// head partials of those pieces in order (lane groups take alternate pieces, then a wave
+// reduction), and applies the update to the row.
+template <typename RowT>
+__global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   typedef typename F32V<EPL>::t V;
-  __shared__ V s_part[kBlock];
-  const int lane = threadIdx.x & ((1 << gs_log2) - 1);
-  const int grp = threadIdx.x >> gs_log2;
-  const int ngrp = kBlock >> gs_log2;
-  const GradT* G = reinterpret_cast<const GradT*>(a.grad);
-  const int F = a.d.n_fields;
-  const int e0 = lane * EPL;
-  const uint32_t n_long = a.ctr[0];
+  const int GS = 1 << gs_log2;
+  const int IPR = 64 >> gs_log2;
+  const int lane = lane_id();
+  const int li = lane & (GS - 1);
+  const int g = lane >> gs_log2;
+  const int e0 = li * EPL;
+  const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
   if (blockIdx.x == 0 && threadIdx.x == 0 && a.n_unique) *a.n_unique = (int64_t)a.ctr[1];
-  for (uint32_t s = blockIdx.x; s < n_long; s += gridDim.x) {
-    const int32_t i0 = (int32_t)a.long_list[s];
-    const uint32_t k = a.key[i0];
-    const uint32_t bag0 = a.val[i0];
-    const int f = (int)(bag0 % (uint32_t)F);
-    const int D = a.d.var_dim ? a.d.fdim[f] : a.d.fixed_dim;
-    const int col = a.d.var_dim ? a.d.fcol[f] : f * a.d.fixed_dim;
-    const GradT* Gc = G + col + e0;
-    V g = 0.0f;
-    if (e0 < D) {
-      int32_t e = i0 + grp;
-      for (;;) {
-        uint32_t bg[4];
-        bool ok[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int32_t x = e + u * ngrp;
-          ok[u] = (x < a.n) && (a.key[x] == k);
-          bg[u] = ok[u] ? a.val[x] : 0u;
-        }
-        V x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          x[u] = ok[u] ? load_f32<GradT, EPL>(Gc + (uint64_t)(bg[u] / (uint32_t)F) * a.d.out_width)
-                       : V(0.0f);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) g += x[u];
-        if (!ok[3]) break;
-        e += 4 * ngrp;
-      }
+  for (int64_t t = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / 64; t < a.n_pieces; t += wstride) {
+    if (!(a.pflag[t] & 1u)) continue;
+    const uint32_t k = a.pkey[2 * t];
+    const int D = (int)a.pkey[2 * t + 1];
+    const bool on = e0 < D;
+    const RowState<EPL> st = (g == 0 && on) ? load_state<RowT, EPL>(a, k, e0) : RowState<EPL>{};
+    V sum = (g == 0 && on) ? load_f32<float, EPL>(a.ptail + t * a.pdim + e0) : V(0.0f);
+    for (int64_t u0 = t + 1; u0 < a.n_pieces; u0 += 64) {
+      // pieces u0 .. u0+63: the chain runs through PASS pieces up to the first END piece
+      const int64_t u = u0 + lane;
+      const uint32_t hk = u < a.n_pieces ? (a.pflag[u] >> 1) & 3u : 0u;
+      const uint64_t stop = __ballot(hk != kHeadPasses);
+      const int last = stop ? __builtin_ctzll(stop) : 63;  // index of the ending piece
+      for (int q = g; q <= last; q += IPR)
+        if (on && u0 + q < a.n_pieces) sum += load_f32<float, EPL>(a.phead + (u0 + q) * a.pdim + e0);
+      if (stop) break;
     }
-    s_part[threadIdx.x] = g;
-    __syncthreads();
-    if (grp == 0 && e0 < D) {
-      V tot = 0.0f;
-      for (int q = 0; q < ngrp; ++q) tot += s_part[(q << gs_log2) + lane];
-      adagrad_row<RowT, EPL>(a, k, e0, tot);
+    // reduce the groups' sums into group 0
+    for (int d = IPR >> 1; d >= 1; d >>= 1) {
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) sum[q] += __shfl_down(sum[q], d * GS, 64);
     }
-    __syncthreads();
+    if (g == 0 && on) apply_state<RowT, EPL>(a, k, e0, sum, st);
   }
 }
 
@@ -582,6 +761,7 @@ struct SegArgs {
   const uint32_t* key;
   int32_t n;
   int32_t tiles;
+  int32_t tile;       // items per tile
   uint32_t miss_key;
   uint32_t* seg;      // [tiles + 1] head counts -> exclusive offsets; [tiles] = U
   uint32_t* headpos;  // [n + 1] position of each head
@@ -599,7 +779,7 @@ __global__ __launch_bounds__(kBlock) void k_seg_count(SegArgs a) {
   __shared__ uint32_t s_c, s_v;
   if (threadIdx.x == 0) { s_c = 0; s_v = 0; }
   __syncthreads();
-  const int32_t i0 = blockIdx.x * kTile, i1 = min(a.n, i0 + kTile);
+  const int32_t i0 = blockIdx.x * a.tile, i1 = min(a.n, i0 + a.tile);
   uint32_t c = 0, v = 0;
   for (int32_t i = i0 + threadIdx.x; i < i1; i += kBlock) {
     c += seg_head(a, i);
@@ -630,9 +810,9 @@ __global__ __launch_bounds__(kBlock) void k_seg_scan(SegArgs a) {
 
 __global__ __launch_bounds__(kBlock) void k_seg_write(SegArgs a) {
   __shared__ uint32_t s_w[kWaves];
-  const int32_t i0 = blockIdx.x * kTile;
+  const int32_t i0 = blockIdx.x * a.tile;
   uint32_t base = a.seg[blockIdx.x];
-  for (int32_t c = 0; c < kTile; c += kBlock) {
+  for (int32_t c = 0; c < a.tile; c += kBlock) {
     const int32_t i = i0 + c + threadIdx.x;
     const bool h = (i < a.n) && seg_head(a, i);
     uint32_t total;
@@ -702,28 +882,72 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
   return hipGetLastError();
 }
 
-BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space) {
+BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t row_f16) {
   BwdPlan p{};
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.n = (int32_t)nnz;
-  p.tiles = (int32_t)((nnz + kTile - 1) / kTile);
-  p.miss_key = rowref_space;
-  int bits = 0;
-  while (bits < 32 && (uint64_t)(p.miss_key >> bits) != 0) ++bits;
-  p.passes = bits <= 8 ? 1 : (bits + 7) / 8;
+  // key bits of the largest rowref; fewest passes of at most 11 bits
+  int keybits = 0;
+  while (keybits < 32 && rowref_space > 1 && ((uint64_t)(rowref_space - 1) >> keybits) != 0) ++keybits;
+  // digit width: each tile's per-bin work (count, scan, offsets) must stay small next to its
+  // per-item work, so wide digits only pay once tiles hold thousands of items
+  const int maxbits = nnz >= (4 << 20) ? 11 : 8;
+  p.passes = keybits <= maxbits ? 1 : (keybits + maxbits - 1) / maxbits;
+  p.bits = (keybits + p.passes - 1) / p.passes;
+  // tiles: enough of them to spread a small batch over every CU, large ones for large batches
+  p.ipt = nnz >= (4 << 20) ? 16 : nnz >= (1 << 20) ? 8 : 4;
+  const int64_t tile = (int64_t)kBlock * p.ipt;
+  p.tiles = (int32_t)((nnz + tile - 1) / tile);
   const size_t n = (size_t)(nnz > 0 ? nnz : 0);
+  const size_t bins = ((size_t)1 << p.bits) + 1;
   size_t o = 0;
   p.off_ka = o; o = al(o + 4 * (n + 1));
   p.off_va = o; o = al(o + 4 * (n + 1));
   p.off_kb = o; o = al(o + 4 * (n + 1));
   p.off_vb = o; o = al(o + 4 * (n + 1));
-  p.off_counts = o; o = al(o + 4 * (size_t)256 * (size_t)(p.tiles > 0 ? p.tiles : 1));
-  p.off_tot = o; o = al(o + 4 * 256);
+  p.off_counts = o; o = al(o + 4 * bins * (size_t)(p.tiles > 0 ? p.tiles : 1));
+  p.off_tot = o; o = al(o + 4 * bins);
   p.off_ctr = o; o = al(o + 4 * 16);
-  p.off_long = o; o = al(o + 4 * (n / (kLong + 1) + 1));
   p.off_seg = o; o = al(o + 4 * ((size_t)p.tiles + 1));
+  // update pieces: about 128k of them (bounded partial traffic), at least one load batch each
+  const int epl = row_f16 ? 8 : 4;
+  p.gsl = log2_group(max_dim, epl);
+  const int ipr = 64 >> p.gsl;
+  const int br = row_f16 ? SegBatch<8>::value : SegBatch<4>::value;
+  int64_t r = (nnz + (int64_t)ipr * 131072 - 1) / ((int64_t)ipr * 131072);
+  r = r < br ? br : r > 16 ? 16 : r;
+  p.rounds = (int32_t)((r + br - 1) / br * br);
+  const int64_t pw = (int64_t)p.rounds * ipr;
+  p.n_pieces = (int32_t)((nnz + pw - 1) / pw);
+  p.pdim = max_dim;
+  const size_t np = (size_t)(p.n_pieces > 0 ? p.n_pieces : 1);
+  p.off_phead = o; o = al(o + 4 * np * (size_t)p.pdim);
+  p.off_ptail = o; o = al(o + 4 * np * (size_t)p.pdim);
+  p.off_pflag = o; o = al(o + 4 * np);
+  p.off_pkey = o; o = al(o + 8 * np);
   p.bytes = o;
   return p;
+}
+
+template <bool FIRST, int IPT>
+static void launch_scatter_ipt(const SortArgs& s, int logb, dim3 grid, hipStream_t st) {
+  const dim3 blk(kBlock);
+  switch (logb) {
+    case 8: hipLaunchKernelGGL((k_sort_scatter<FIRST, IPT, 8>), grid, blk, 0, st, s); break;
+    case 9: hipLaunchKernelGGL((k_sort_scatter<FIRST, IPT, 9>), grid, blk, 0, st, s); break;
+    case 10: hipLaunchKernelGGL((k_sort_scatter<FIRST, IPT, 10>), grid, blk, 0, st, s); break;
+    default: hipLaunchKernelGGL((k_sort_scatter<FIRST, IPT, 11>), grid, blk, 0, st, s); break;
+  }
+}
+
+template <bool FIRST>
+static void launch_scatter(const SortArgs& s, int ipt, int logb, dim3 grid, hipStream_t st) {
+  switch (ipt) {
+    case 2: launch_scatter_ipt<FIRST, 2>(s, logb, grid, st); break;
+    case 4: launch_scatter_ipt<FIRST, 4>(s, logb, grid, st); break;
+    case 8: launch_scatter_ipt<FIRST, 8>(s, logb, grid, st); break;
+    default: launch_scatter_ipt<FIRST, 16>(s, logb, grid, st); break;
+  }
 }
 
 hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ctx) {
@@ -745,15 +969,19 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   s.ctr = ctr;
   s.n = p.n;
   s.tiles = p.tiles;
-  s.miss_key = p.miss_key;
+  s.tile = kBlock * p.ipt;
+  s.rowref_space = a.d.rowref_space;
+  s.bits = p.bits;
+  const int logb = p.bits <= 8 ? 8 : p.bits;
   uint32_t* ka = reinterpret_cast<uint32_t*>(ws + p.off_ka);
   uint32_t* va = reinterpret_cast<uint32_t*>(ws + p.off_va);
   uint32_t* kb = reinterpret_cast<uint32_t*>(ws + p.off_kb);
   uint32_t* vb = reinterpret_cast<uint32_t*>(ws + p.off_vb);
   const dim3 tiles(p.tiles), blk(kBlock);
+  const dim3 nbins((1u << p.bits) + 1);
   uint32_t *src_k = nullptr, *src_v = nullptr, *dst_k = ka, *dst_v = va;
   for (int pass = 0; pass < p.passes; ++pass) {
-    s.shift = 8 * pass;
+    s.shift = p.bits * pass;
     s.kin = src_k;
     s.vin = src_v;
     s.kout = dst_k;
@@ -765,12 +993,12 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
     }
     {
       KTimer tm(ctx, "sort_scan");
-      hipLaunchKernelGGL(k_sort_scan, dim3(256), blk, 0, ctx.stream, s, pass == 0 ? 1 : 0);
+      hipLaunchKernelGGL(k_sort_scan, nbins, blk, 0, ctx.stream, s, pass == 0 ? 1 : 0);
     }
     {
       KTimer tm(ctx, "sort_scatter");
-      if (pass == 0) hipLaunchKernelGGL(k_sort_scatter<true>, tiles, blk, 0, ctx.stream, s);
-      else hipLaunchKernelGGL(k_sort_scatter<false>, tiles, blk, 0, ctx.stream, s);
+      if (pass == 0) launch_scatter<true>(s, p.ipt, logb, tiles, ctx.stream);
+      else launch_scatter<false>(s, p.ipt, logb, tiles, ctx.stream);
     }
     src_k = dst_k;
     src_v = dst_v;
@@ -785,39 +1013,36 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   u.key = src_k;
   u.val = src_v;
   u.n = p.n;
-  u.miss_key = p.miss_key;
+  u.miss_key = kMissKey;
   u.grad = a.grad;
   u.lr = a.lr;
   u.eps = a.eps;
   u.ctr = ctr;
-  u.long_list = reinterpret_cast<uint32_t*>(ws + p.off_long);
   u.n_unique = a.n_unique;
-  const int epl = a.d.row_f16 ? 8 : 4;
-  const int gsl = log2_group(a.d.max_dim, epl);
-  const int64_t groups = ((int64_t)p.n + kQ - 1) / kQ;
-  const int64_t per_block = kBlock >> gsl;
-  const dim3 gshort((unsigned)((groups + per_block - 1) / per_block));
-  const int64_t max_long = (int64_t)p.n / (kLong + 1) + 1;
-  const dim3 glong((unsigned)(max_long < 4096 ? max_long : 4096));
+  u.rounds = p.rounds;
+  u.n_pieces = p.n_pieces;
+  u.pdim = p.pdim;
+  u.phead = reinterpret_cast<float*>(ws + p.off_phead);
+  u.ptail = reinterpret_cast<float*>(ws + p.off_ptail);
+  u.pflag = reinterpret_cast<uint32_t*>(ws + p.off_pflag);
+  u.pkey = reinterpret_cast<uint32_t*>(ws + p.off_pkey);
+  const int gsl = p.gsl;
+  const int64_t blocks = ((int64_t)p.n_pieces + (kBlock / 64) - 1) / (kBlock / 64);
+  const dim3 gpiece((unsigned)(blocks < 8192 ? blocks : 8192));
   {
-    KTimer tm(ctx, "update_short");
+    KTimer tm(ctx, "update_pieces");
     if (a.d.row_f16) {
-      if (a.grad_f16) hipLaunchKernelGGL((k_update_short<_Float16, _Float16>), gshort, blk, 0, ctx.stream, u, gsl);
-      else hipLaunchKernelGGL((k_update_short<_Float16, float>), gshort, blk, 0, ctx.stream, u, gsl);
+      if (a.grad_f16) hipLaunchKernelGGL((k_update_pieces<_Float16, _Float16>), gpiece, blk, 0, ctx.stream, u, gsl);
+      else hipLaunchKernelGGL((k_update_pieces<_Float16, float>), gpiece, blk, 0, ctx.stream, u, gsl);
     } else {
-      if (a.grad_f16) hipLaunchKernelGGL((k_update_short<float, _Float16>), gshort, blk, 0, ctx.stream, u, gsl);
-      else hipLaunchKernelGGL((k_update_short<float, float>), gshort, blk, 0, ctx.stream, u, gsl);
+      if (a.grad_f16) hipLaunchKernelGGL((k_update_pieces<float, _Float16>), gpiece, blk, 0, ctx.stream, u, gsl);
+      else hipLaunchKernelGGL((k_update_pieces<float, float>), gpiece, blk, 0, ctx.stream, u, gsl);
     }
   }
   {
-    KTimer tm(ctx, "update_long");
-    if (a.d.row_f16) {
-      if (a.grad_f16) hipLaunchKernelGGL((k_update_long<_Float16, _Float16>), glong, blk, 0, ctx.stream, u, gsl);
-      else hipLaunchKernelGGL((k_update_long<_Float16, float>), glong, blk, 0, ctx.stream, u, gsl);
-    } else {
-      if (a.grad_f16) hipLaunchKernelGGL((k_update_long<float, _Float16>), glong, blk, 0, ctx.stream, u, gsl);
-      else hipLaunchKernelGGL((k_update_long<float, float>), glong, blk, 0, ctx.stream, u, gsl);
-    }
+    KTimer tm(ctx, "update_fixup");
+    if (a.d.row_f16) hipLaunchKernelGGL((k_update_fixup<_Float16>), gpiece, blk, 0, ctx.stream, u, gsl);
+    else hipLaunchKernelGGL((k_update_fixup<float>), gpiece, blk, 0, ctx.stream, u, gsl);
   }
   err = hipGetLastError();
   if (err != hipSuccess || !a.unique) return err;
@@ -826,7 +1051,8 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   g.key = src_k;
   g.n = p.n;
   g.tiles = p.tiles;
-  g.miss_key = p.miss_key;
+  g.tile = kBlock * p.ipt;
+  g.miss_key = kMissKey;
   g.seg = reinterpret_cast<uint32_t*>(ws + p.off_seg);
   g.headpos = dst_k;  // the spare key buffer (n + 1 words)
   g.unique = a.unique;

@@ -25,7 +25,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "embedding rows looked up+updated/sec (fwd+bwd) and achieved HBM GB/s vs peak"
-LONG_SEGMENT = 32          # occurrences above which a row takes the library's block path
 KERNEL_SRC = os.path.join(ROOT, "ad_recommendation_amd", "csrc", "emb_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -40,27 +39,55 @@ def kernel_src_hash() -> str:
 
 
 # --------------------------------------------------------------------------- byte model
-def batch_stats(w, bt, dims):
-    """Per-batch counts the byte model needs (host side, from the generated batch)."""
-    keys = bt["keys"]
+def piece_plan(nnz, max_dim, row_f16):
+    """Lane-group size and piece length of the library's update kernels."""
+    epl = 8 if row_f16 else 4
+    lanes, gsl = (max_dim + epl - 1) // epl, 0
+    while (1 << gsl) < lanes:
+        gsl += 1
+    ipr = 64 >> gsl
+    br = 2 if row_f16 else 4
+    r = (nnz + ipr * 131072 - 1) // (ipr * 131072)
+    r = min(max(r, br), 16)
+    rounds = (r + br - 1) // br * br
+    return rounds * ipr, (nnz + rounds * ipr - 1) // (rounds * ipr)
+
+
+def batch_stats(w, bt, dims, rowref):
+    """Per-batch counts the byte model needs, from the batch and the rows its keys resolve to."""
     off = bt["offsets"]
     F = w.n_fields
     bag = np.repeat(np.arange(off.size - 1, dtype=np.int64), np.diff(off.astype(np.int64)))
     width = dims[bag % F].astype(np.int64)           # row width of each occurrence
-    u, inv, cnt = np.unique(keys, return_inverse=True, return_counts=True)
-    uw = np.zeros(u.size, dtype=np.int64)
-    uw[inv] = width
-    long_u = cnt > LONG_SEGMENT
-    occ_long = long_u[inv]
+    rr = rowref.astype(np.int64)
+    order = np.argsort(rr, kind="stable")
+    srr = rr[order]
+    sw = width[order]
+    heads = np.concatenate([[True], srr[1:] != srr[:-1]])
+    starts = np.nonzero(heads)[0]
+    ends = np.concatenate([starts[1:], [srr.size]]) - 1
+    pw, n_pieces = piece_plan(srr.size, int(dims.max()), w.row_dtype == "f16")
+    cross = (starts // pw) != (ends // pw)          # finished by the fixup kernel
+    uw = sw[starts]
     return {
-        "nnz": int(keys.size), "U": int(u.size), "bags": int(off.size - 1),
+        "nnz": int(rr.size), "U": int(starts.size), "bags": int(off.size - 1),
         "occ_elems": int(width.sum()),                      # sum of D over occurrences
         "bag_elems": int(dims.sum()) * (off.size - 1) // F,  # sum of D over bags
-        "u_elems_short": int(uw[~long_u].sum()), "u_elems_long": int(uw[long_u].sum()),
-        "occ_short": int((~occ_long).sum()), "occ_long": int(occ_long.sum()),
-        "occ_elems_short": int(width[~occ_long].sum()), "occ_elems_long": int(width[occ_long].sum()),
-        "u_long": int(long_u.sum()),
+        "u_elems_inside": int(uw[~cross].sum()), "u_elems_cross": int(uw[cross].sum()),
+        "u_cross": int(cross.sum()), "n_pieces": int(n_pieces), "pdim": int(dims.max()),
     }
+
+
+def sort_plan(nnz, rowref_space):
+    """Items per thread, tiles and digit bits of the library's radix sort for a batch."""
+    keybits = 0
+    while keybits < 32 and rowref_space > 1 and ((rowref_space - 1) >> keybits) != 0:
+        keybits += 1
+    maxbits = 11 if nnz >= (4 << 20) else 8
+    passes = 1 if keybits <= maxbits else (keybits + maxbits - 1) // maxbits
+    bits = (keybits + passes - 1) // passes
+    ipt = 16 if nnz >= (4 << 20) else 8 if nnz >= (1 << 20) else 4
+    return ipt, (nnz + 256 * ipt - 1) // (256 * ipt), bits
 
 
 def kernel_bytes(name, st, w, passes):
@@ -78,14 +105,18 @@ def kernel_bytes(name, st, w, passes):
     if name == "sort_hist":
         return n * 4
     if name == "sort_scan":
-        tiles = (n + 2047) // 2048
-        return 256 * tiles * 8
+        ipt, tiles, bits = sort_plan(n, passes)
+        return ((1 << bits) + 1) * tiles * 8
     if name == "sort_scatter":
         return n * 16 / 1.0
-    if name == "update_short":
-        return st["occ_short"] * 8 + st["occ_elems_short"] * sg + st["u_elems_short"] * state
-    if name == "update_long":
-        return st["occ_long"] * 8 + st["occ_elems_long"] * sg + st["u_elems_long"] * state
+    if name == "update_pieces":
+        # every occurrence's sorted pair and gradient slice; rows finished inside a piece;
+        # head/tail partials of pieces whose segments cross
+        return (n * 8 + st["occ_elems"] * sg + st["u_elems_inside"] * state
+                + st["u_cross"] * 2 * st["pdim"] * 4 + st["n_pieces"] * 12)
+    if name == "update_fixup":
+        return st["n_pieces"] * 4 + st["u_cross"] * (8 + 2 * st["pdim"] * 4) + \
+            st["u_elems_cross"] * state
     return 0
 
 
@@ -190,7 +221,8 @@ def main():
     ws_bytes = 0
     for b in range(R):
         bt = synth.batch(w, b)
-        st = batch_stats(w, bt, dims)
+        rr, _ = emb.table_key_rowref(T.h, bt["keys"])
+        st = batch_stats(w, bt, dims, rr)
         n_bags = bt["offsets"].size - 1
         ring.append({
             "keys": torch.from_numpy(bt["keys"]).to(dev),
@@ -203,9 +235,7 @@ def main():
         ws_bytes = max(ws_bytes, emb.bwd_workspace_bytes(T.h, n_bags, st["nnz"]))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     n_unique = torch.zeros(R, dtype=torch.int64, device=dev)
-    passes = 0
-    while passes < 4 and (T.info["rowref_space"] >> (8 * passes)) > 0:
-        passes += 1
+    passes = T.info["rowref_space"]
     log(f"[bench] ring of {R} batches staged; mean nnz {np.mean([r['nnz'] for r in ring]):.0f}, "
         f"mean unique {np.mean([r['st']['U'] for r in ring]):.0f}")
 

@@ -21,6 +21,8 @@
  *     thread-local message for the last failure on the calling thread.
  *   - "d_" pointers are device pointers (HBM), owned by the caller; the hot-path entry points never
  *     allocate device memory.  Host pointers passed to a function are only read during the call.
+ *   - Device buffers read or written with vector accesses (d_out, d_rowref, d_grad, d_ws) must be
+ *     16-byte aligned (EMB_EINVAL otherwise); torch allocations are.
  *   - Device work is enqueued on the caller's stream (a hipStream_t passed as void*, NULL = the null
  *     stream) and is asynchronous unless a function says it synchronises.
  *   - A table object is not thread-safe; distinct tables are independent.

@@ -133,14 +133,18 @@ def test_call_errors_without_device_work():
     T, keys, _, _ = _table(W.TINY)
     L = emb.lib()
     nul = None
+    A = 1 << 20   # a fake, 16-byte aligned "device" address: no call below reaches the device
     # lookup arguments are checked before the table state
-    assert L.lookup_pool_fwd(T.h, 8, 8, 4, 4, 8, 7, 8, nul, nul, nul) == -1       # bad out dtype
-    assert L.lookup_pool_fwd(T.h, nul, 8, 4, 4, 8, 0, 8, nul, nul, nul) == -1     # null keys
-    assert L.lookup_pool_fwd(T.h, 8, 8, -1, 4, 8, 0, 8, nul, nul, nul) == -1      # negative size
-    assert L.lookup_pool_fwd(T.h, 8, 8, 4, 4, 8, 0, 8, nul, nul, nul) == -6       # before flash
-    assert L.sparse_adagrad_bwd(T.h, 8, 8, 4, 4, 8, 0, 0.1, 1e-8, 8, 16, nul, nul, nul, nul) == -5  # ws too small
-    assert L.sparse_adagrad_bwd(T.h, 8, 8, 4, 4, 8, 0, 0.1, 1e-8, 8, 1 << 20, nul, 8, nul, nul) == -1  # count w/o unique
-    assert L.sparse_adagrad_bwd(T.h, 8, 8, 4, 4, 8, 0, 0.1, 1e-8, 8, 1 << 20, nul, nul, nul, nul) == -6
+    assert L.lookup_pool_fwd(T.h, A, A, 4, 4, A, 7, A, nul, nul, nul) == -1       # bad out dtype
+    assert L.lookup_pool_fwd(T.h, nul, A, 4, 4, A, 0, A, nul, nul, nul) == -1     # null keys
+    assert L.lookup_pool_fwd(T.h, A, A, -1, 4, A, 0, A, nul, nul, nul) == -1      # negative size
+    assert L.lookup_pool_fwd(T.h, A, A, 4, 4, A + 8, 0, A, nul, nul, nul) == -1   # misaligned out
+    assert L.lookup_pool_fwd(T.h, A, A, 0, 4, A, 0, A, nul, nul, nul) == -1       # occurrences, no bags
+    assert L.lookup_pool_fwd(T.h, A, A, 4, 4, A, 0, A, nul, nul, nul) == -6       # before flash
+    assert L.sparse_adagrad_bwd(T.h, A, A, 4, 4, A, 0, 0.1, 1e-8, A, 16, nul, nul, nul, nul) == -5  # ws too small
+    assert L.sparse_adagrad_bwd(T.h, A, A, 4, 4, A, 0, 0.1, 1e-8, A, 1 << 20, nul, A, nul, nul) == -1  # count w/o unique
+    assert L.sparse_adagrad_bwd(T.h, A, A, 4, 4, A + 4, 0, 0.1, 1e-8, A, 1 << 20, nul, nul, nul, nul) == -1  # misaligned grad
+    assert L.sparse_adagrad_bwd(T.h, A, A, 4, 4, A, 0, 0.1, 1e-8, A, 1 << 20, nul, nul, nul, nul) == -6
     assert L.pass_flash(T.h, 256, 16, nul) == -5                                    # arena too small
     assert L.pass_flash(T.h, 100, 1 << 40, nul) == -1                               # misaligned
     assert L.pass_writeback(T.h, nul) == -6
