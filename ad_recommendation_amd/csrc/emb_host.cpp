@@ -233,6 +233,11 @@ struct EmbTable {
     d.fcol = meta + F;
     d.fgran = meta + 2 * F;
     d.rowref_space = rowref_space;
+    // division by the field count as a multiply and shift (exact for dividends below 2^31)
+    int l = 0;
+    while ((1u << l) < (uint32_t)F) ++l;
+    d.fdiv_s = 31 + l;
+    d.fdiv_m = (uint32_t)(((1ull << d.fdiv_s) + (uint64_t)F - 1) / (uint64_t)F);
     return d;
   }
 
@@ -415,7 +420,9 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
   T->off_acc = align256(T->off_rows + T->total_elems * eb);
   T->off_master = align256(T->off_acc + T->total_elems * 4);
   T->off_meta = align256(T->off_master + (T->has_master ? T->total_elems * 4 : 0));
-  T->arena_bytes = align256(T->off_meta + 3 * 4 * (size_t)T->F);
+  // 4 KiB of tail padding: kernels read row 0 (+ lane offset) in place of a masked-off row, which
+  // must stay inside the arena even for an empty table
+  T->arena_bytes = align256(T->off_meta + 3 * 4 * (size_t)T->F) + 4096;
   if (T->flags & EMB_FLAG_PINNED_STAGING) {
     hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&T->image), T->arena_bytes, 0);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the host image");

@@ -55,6 +55,8 @@ struct DevDesc {
   const int32_t* fcol;   // [F] first pooled column per field
   const int32_t* fgran;  // [F] rowref units per row of the field
   uint32_t rowref_space; // rowref values are < rowref_space
+  uint32_t fdiv_m;       // n / n_fields == (n * fdiv_m) >> fdiv_s for every n < 2^31
+  int32_t fdiv_s;
 };
 
 // Kernel timing: events bracket each launch when enabled.

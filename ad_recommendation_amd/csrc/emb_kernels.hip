@@ -10,6 +10,8 @@
 // Everything is memory-bound: no matrix cores, 16-byte vector loads, LDS for tile staging.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "emb_internal.h"
 
 namespace emb {
@@ -45,6 +47,17 @@ template <typename T, int N>
 __device__ __forceinline__ void store_from_f32(T* p, typename F32V<N>::t x) {
   typedef typename VecOf<T, N>::t V;
   *reinterpret_cast<V*>(p) = __builtin_convertvector(x, V);
+}
+
+// Raw vector loads: every gather in a hot loop is issued unconditionally (masked-off lanes read a
+// valid stand-in address) and converted only after the whole batch of loads is in flight.
+template <typename T, int N>
+__device__ __forceinline__ typename VecOf<T, N>::t load_raw(const T* p) {
+  return *reinterpret_cast<const typename VecOf<T, N>::t*>(p);
+}
+template <typename T, int N>
+__device__ __forceinline__ typename F32V<N>::t to_f32(typename VecOf<T, N>::t v) {
+  return __builtin_convertvector(v, typename F32V<N>::t);
 }
 
 // ---------------------------------------------------------------- wave / block helpers
@@ -92,9 +105,14 @@ __device__ __forceinline__ TabSel pick_tab(const DevDesc& d, uint64_t key) {
   return s;
 }
 
+__device__ __forceinline__ uint32_t div_fields(const DevDesc& d, uint32_t n) {
+  return (uint32_t)(((uint64_t)n * d.fdiv_m) >> d.fdiv_s);
+}
+
 // Ordered linear probing over 128-byte buckets of 15 keys: scan from the home slot until the key
 // or an empty slot.  On a hit the rowref is the bucket's stored prefix plus the row units of the
 // occupied slots before the hit (rows are stored in slot order).
+template <bool VAR>
 __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, int bag_field,
                                               int64_t& slot) {
   slot = -1;
@@ -122,14 +140,17 @@ __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, in
       if (!((match >> l) & 1u)) return kMiss;
       const uint32_t below = occ & ((1u << l) - 1u);
       uint32_t rr = (uint32_t)v[7].y;  // word 15: rowref prefix of the bucket
-      if (!d.var_dim) {
+      if (!VAR) {
         rr += __builtin_popcount(below);
       } else {
+        uint32_t gq[kKeysPerBucket];
 #pragma unroll
         for (int q = 0; q < kKeysPerBucket; ++q) {
           const uint64_t w = (q & 1) ? v[q >> 1].y : v[q >> 1].x;
-          if ((below >> q) & 1u) rr += (uint32_t)d.fgran[(int)(w >> 48)];
+          gq[q] = (uint32_t)d.fgran[((below >> q) & 1u) ? (int)(w >> 48) : 0];
         }
+#pragma unroll
+        for (int q = 0; q < kKeysPerBucket; ++q) rr += ((below >> q) & 1u) ? gq[q] : 0u;
       }
       slot = (int64_t)b * kKeysPerBucket + l;
       return rr;
@@ -143,9 +164,33 @@ __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, in
 constexpr int kFwdBags = 64;     // bags per block
 constexpr int kFwdKeyCap = 2048; // rowrefs staged in LDS; larger blocks re-read them from HBM/L2
 
-template <typename RowT, typename OutT>
+// Gathers and sums the rows of bag jb's occurrences k0..k1 (rowrefs from `rr`), EPL elements per
+// lane, four rows in flight; misses read row 0 and are dropped.
+template <typename RowT, typename RR>
+__device__ __forceinline__ typename F32V<16 / sizeof(RowT)>::t pool_rows(const DevDesc& d, RR rr,
+                                                                         int k0, int k1, int e0) {
+  constexpr int EPL = 16 / (int)sizeof(RowT);
+  typedef typename F32V<EPL>::t AccV;
+  typedef typename VecOf<RowT, EPL>::t Raw;
+  const RowT* rows = reinterpret_cast<const RowT*>(d.rows) + e0;
+  AccV acc = 0.0f;
+  for (int k = k0; k < k1; k += 4) {
+    uint32_t r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = k + u < k1 ? rr(k + u) : kMiss;
+    Raw x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      x[u] = load_raw<RowT, EPL>(rows + (r[u] != kMiss ? (uint64_t)r[u] * d.granule : 0ull));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += r[u] != kMiss ? to_f32<RowT, EPL>(x[u]) : AccV(0.0f);
+  }
+  return acc;
+}
+
+template <typename RowT, typename OutT, bool VAR>
 __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2) {
-  constexpr int EPL = 16 / (int)sizeof(RowT);  // row elements per lane: one 16-byte load
+  constexpr int EPL = 16 / (int)sizeof(RowT);
   typedef typename F32V<EPL>::t AccV;
   __shared__ int32_t s_off[kFwdBags + 1];
   __shared__ uint32_t s_rr[kFwdKeyCap];
@@ -161,7 +206,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   const int32_t nk = max(s_off[nb] - base, 0);
   const bool in_lds = nk <= kFwdKeyCap;
   const int F = a.d.n_fields;
-  const int f0 = j0 % F;
+  const int f0 = (int)((uint32_t)j0 - div_fields(a.d, (uint32_t)j0) * (uint32_t)F);
 
   // phase 1: one lane per key
   uint32_t miss = 0;
@@ -173,8 +218,10 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
       const int mid = (lo + hi + 1) >> 1;
       if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
     }
+    int bf = f0 + lo;
+    bf = bf >= F ? bf - (int)div_fields(a.d, (uint32_t)bf) * F : bf;
     int64_t sl;
-    const uint32_t rr = probe_key(a.d, key, (f0 + lo) % F, sl);
+    const uint32_t rr = probe_key<VAR>(a.d, key, bf, sl);
     miss += (rr == kMiss);
     if (in_lds) s_rr[i] = rr;
     a.rowref[pos] = rr;
@@ -187,35 +234,21 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   // phase 2: a group of 2^gs_log2 lanes per bag, EPL elements per lane
   const int lane = tid & ((1 << gs_log2) - 1);
   const int ngrp = kBlock >> gs_log2;
-  const RowT* rows = reinterpret_cast<const RowT*>(a.d.rows);
   OutT* out = reinterpret_cast<OutT*>(a.out);
+  const int e0 = lane * EPL;
   for (int jb = tid >> gs_log2; jb < nb; jb += ngrp) {
-    const int f = (f0 + jb) % F;
-    const int D = a.d.var_dim ? a.d.fdim[f] : a.d.fixed_dim;
-    const int col = a.d.var_dim ? a.d.fcol[f] : f * a.d.fixed_dim;
-    const int e0 = lane * EPL;
+    int f = f0 + jb;
+    f = f >= F ? f - (int)div_fields(a.d, (uint32_t)f) * F : f;
+    const int D = VAR ? a.d.fdim[f] : a.d.fixed_dim;
+    const int col = VAR ? a.d.fcol[f] : f * a.d.fixed_dim;
     if (e0 >= D) continue;
-    const int32_t b = (j0 + jb) / F;
+    const uint32_t b = div_fields(a.d, (uint32_t)(j0 + jb));
     const int k0 = min(max(s_off[jb] - base, 0), nk), k1 = min(max(s_off[jb + 1] - base, k0), nk);
-    AccV acc = 0.0f;
-    int k = k0;
-    for (; k + 4 <= k1; k += 4) {
-      uint32_t r[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = in_lds ? s_rr[k + u] : a.rowref[base + k + u];
-      AccV x[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        x[u] = (r[u] != kMiss)
-                   ? load_f32<RowT, EPL>(rows + (uint64_t)r[u] * a.d.granule + e0)
-                   : AccV(0.0f);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc += x[u];
-    }
-    for (; k < k1; ++k) {
-      const uint32_t r = in_lds ? s_rr[k] : a.rowref[base + k];
-      if (r != kMiss) acc += load_f32<RowT, EPL>(rows + (uint64_t)r * a.d.granule + e0);
-    }
+    AccV acc;
+    if (in_lds)
+      acc = pool_rows<RowT>(a.d, [&](int k) { return s_rr[k]; }, k0, k1, e0);
+    else
+      acc = pool_rows<RowT>(a.d, [&](int k) { return a.rowref[base + k]; }, k0, k1, e0);
     store_from_f32<OutT, EPL>(out + (uint64_t)b * a.d.out_width + col + e0, acc);
   }
 }
@@ -291,24 +324,29 @@ __global__ __launch_bounds__(kBlock) void k_sort_hist(SortArgs a) {
   const int bins = (1 << a.bits) + 1;
   for (int d = threadIdx.x; d < bins; d += kBlock) h[d] = 0;
   __syncthreads();
-  const int per = a.tile / kBlock;  // a multiple of 4
+  const int per = a.tile / kBlock;  // 4, 8 or 16
   const int32_t i0 = t * a.tile + (int32_t)threadIdx.x * per;
   const uint32_t* src = FIRST ? a.rowref : a.kin;
-  uint32_t prev = 0xFFFFFFFFu, run = 0;
-  for (int u = 0; u < per; u += 4) {
-    const int32_t i = i0 + u;
-    uint32_t k4[4];
-    if (i + 3 < a.n) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + i);
-      k4[0] = v.x; k4[1] = v.y; k4[2] = v.z; k4[3] = v.w;
-    } else {
+  const bool full = (int64_t)(t + 1) * a.tile <= a.n;  // every tile but possibly the last
+  uint32_t k16[16];
+  if (full) {
+    // all of this thread's items first, then the counting
 #pragma unroll
-      for (int q = 0; q < 4; ++q) k4[q] = i + q < a.n ? src[i + q] : 0u;
+    for (int u = 0; u < 16; u += 4) {
+      if (u < per) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + i0 + u);
+        k16[u] = v.x; k16[u + 1] = v.y; k16[u + 2] = v.z; k16[u + 3] = v.w;
+      }
     }
+  } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (i + q >= a.n) break;
-      const uint32_t k = FIRST ? sort_key_of(k4[q], a.rowref_space) : k4[q];
+    for (int u = 0; u < 16; ++u) k16[u] = (u < per && i0 + u < a.n) ? src[i0 + u] : 0u;
+  }
+  uint32_t prev = 0xFFFFFFFFu, run = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    if (u < per && i0 + u < a.n) {
+      const uint32_t k = FIRST ? sort_key_of(k16[u], a.rowref_space) : k16[u];
       const uint32_t dg = digit_of(k, a.shift, a.bits);
       if (dg != prev) {
         if (run) atomicAdd(&h[prev], run);
@@ -423,6 +461,14 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
 
   uint32_t key[IPT], val[IPT], rank[IPT];
   const uint64_t lt = (1ull << lane) - 1ull;
+  // all of this thread's items first (masked-off items read item 0), then the ranking
+#pragma unroll
+  for (int k = 0; k < IPT; ++k) {
+    const int32_t li = w * (IPT * 64) + k * 64 + lane;
+    const int32_t i = li < tn ? i0 + li : 0;
+    key[k] = FIRST ? a.rowref[i] : a.kin[i];
+    val[k] = FIRST ? 0u : a.vin[i];
+  }
 #pragma unroll
   for (int k = 0; k < IPT; ++k) {
     const int32_t li = w * (IPT * 64) + k * 64 + lane;  // item index inside the tile
@@ -431,7 +477,7 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
     uint32_t kk = 0, vv = 0;
     if (valid) {
       if (FIRST) {
-        kk = sort_key_of(a.rowref[i], a.rowref_space);
+        kk = sort_key_of(key[k], a.rowref_space);
         if (stage) {
           int lo = 0, hi = nst - 2;
           while (lo < hi) {
@@ -443,8 +489,8 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
           vv = (uint32_t)bag_search_global(a.offsets, jlo, a.n_bags - 1, i);
         }
       } else {
-        kk = a.kin[i];
-        vv = a.vin[i];
+        kk = key[k];
+        vv = val[k];
       }
     }
     const uint32_t dg = digit_of(kk, a.shift, a.bits);
@@ -516,57 +562,60 @@ struct UpdArgs {
   uint32_t* pkey;        // [n_pieces][2] row and width of the tail partial's segment
 };
 
-// Row state of one lane's EPL elements, read ahead of the update.
-template <int EPL>
-struct RowState {
-  typename F32V<EPL>::t acc, w;
+// Row state of one lane's EPL elements as loaded: the accumulator, and the weights the update
+// reads (the fp32 master copy when the table keeps one, else the row itself).
+template <typename RowT, int EPL, bool MASTER>
+struct RawState {
+  typedef typename std::conditional<MASTER, float, RowT>::type WT;
+  typename VecOf<float, EPL>::t acc;
+  typename VecOf<WT, EPL>::t w;
 };
 
-template <typename RowT, int EPL>
-__device__ __forceinline__ RowState<EPL> load_state(const UpdArgs& a, uint32_t r, int e0) {
-  RowState<EPL> st;
-  const uint64_t e = (uint64_t)r * a.d.granule + e0;
-  st.acc = load_f32<float, EPL>(a.d.acc + e);
-  if (sizeof(RowT) == 2 && a.d.has_master) st.w = load_f32<float, EPL>(a.d.master + e);
-  else st.w = load_f32<RowT, EPL>(reinterpret_cast<const RowT*>(a.d.rows) + e);
+// Issues the state loads of row r (row 0 stands in when `on` is false).
+template <typename RowT, int EPL, bool MASTER>
+__device__ __forceinline__ RawState<RowT, EPL, MASTER> load_state(const UpdArgs& a, uint32_t r,
+                                                                  int e0, bool on) {
+  typedef typename RawState<RowT, EPL, MASTER>::WT WT;
+  RawState<RowT, EPL, MASTER> st;
+  const uint64_t e = (on ? (uint64_t)r * a.d.granule : 0ull) + e0;
+  st.acc = load_raw<float, EPL>(a.d.acc + e);
+  st.w = MASTER ? load_raw<WT, EPL>(reinterpret_cast<const WT*>(a.d.master) + e)
+                : load_raw<WT, EPL>(reinterpret_cast<const WT*>(a.d.rows) + e);
   return st;
 }
 
 // Element-wise Adagrad on one lane's elements: acc += g^2; w -= lr * g / (sqrt(acc) + eps).
 // fp16 rows with a master copy update the master and store its fp16 rounding as the row.
-template <typename RowT, int EPL>
+template <typename RowT, int EPL, bool MASTER>
 __device__ __forceinline__ void apply_state(const UpdArgs& a, uint32_t r, int e0,
-                                            typename F32V<EPL>::t g, RowState<EPL> st) {
+                                            typename F32V<EPL>::t g,
+                                            const RawState<RowT, EPL, MASTER>& st) {
   typedef typename F32V<EPL>::t V;
+  typedef typename RawState<RowT, EPL, MASTER>::WT WT;
   const uint64_t e = (uint64_t)r * a.d.granule + e0;
-  const V acc = st.acc + g * g;
+  const V acc = to_f32<float, EPL>(st.acc) + g * g;
   V den;
 #pragma unroll
   for (int q = 0; q < EPL; ++q) den[q] = __builtin_sqrtf(acc[q]) + a.eps;
-  const V w = st.w - (a.lr * g) / den;
+  const V w = to_f32<WT, EPL>(st.w) - (a.lr * g) / den;
   store_from_f32<float, EPL>(a.d.acc + e, acc);
-  RowT* rows = reinterpret_cast<RowT*>(a.d.rows);
-  if (sizeof(RowT) == 2 && a.d.has_master) store_from_f32<float, EPL>(a.d.master + e, w);
-  store_from_f32<RowT, EPL>(rows + e, w);
+  if (MASTER) store_from_f32<float, EPL>(a.d.master + e, w);
+  store_from_f32<RowT, EPL>(reinterpret_cast<RowT*>(a.d.rows) + e, w);
 }
 
-template <typename RowT, int EPL>
-__device__ __forceinline__ void adagrad_row(const UpdArgs& a, uint32_t r, int e0,
-                                            typename F32V<EPL>::t g) {
-  apply_state<RowT, EPL>(a, r, e0, g, load_state<RowT, EPL>(a, r, e0));
-}
-
-template <typename GradT, int EPL>
-__device__ __forceinline__ typename F32V<EPL>::t grad_slice(const UpdArgs& a, uint32_t bag,
-                                                            int e0, int& D) {
-  typedef typename F32V<EPL>::t V;
-  const int F = a.d.n_fields;
-  const int f = (int)(bag % (uint32_t)F);
-  D = a.d.var_dim ? a.d.fdim[f] : a.d.fixed_dim;
-  if (e0 >= D) return V(0.0f);
-  const int col = a.d.var_dim ? a.d.fcol[f] : f * a.d.fixed_dim;
-  const GradT* G = reinterpret_cast<const GradT*>(a.grad);
-  return load_f32<GradT, EPL>(G + (uint64_t)(bag / (uint32_t)F) * a.d.out_width + col + e0);
+// Issues the load of one occurrence's upstream-gradient slice (bag `bag`, lane elements from e0);
+// returns the raw slice, the row width D of the bag's field and whether the lane is in use.
+template <typename GradT, int EPL, bool VAR>
+__device__ __forceinline__ typename VecOf<GradT, EPL>::t grad_raw(const UpdArgs& a, uint32_t bag,
+                                                                  int e0, bool on, int& D,
+                                                                  bool& ok) {
+  const uint32_t b = div_fields(a.d, bag);
+  const int f = (int)(bag - b * (uint32_t)a.d.n_fields);
+  D = VAR ? a.d.fdim[f] : a.d.fixed_dim;
+  const int col = VAR ? a.d.fcol[f] : f * a.d.fixed_dim;
+  ok = on && e0 < D;
+  const GradT* G = reinterpret_cast<const GradT*>(a.grad) + e0;
+  return load_raw<GradT, EPL>(G + (ok ? (uint64_t)b * a.d.out_width + col : 0ull));
 }
 
 // Segmented inclusive scan of one round across the wave's lane groups.  Segments are runs of
@@ -612,87 +661,111 @@ template <int EPL> struct SegBatch { static constexpr int value = EPL == 4 ? 4 :
 
 constexpr uint32_t kHeadEnds = 1u, kHeadPasses = 2u;
 
+constexpr int kPieceMax = 256;  // occurrences per update piece, at most
+
 // Segmented gradient reduction in sorted order fused with the Adagrad update.  Each wave owns
 // pieces of `rounds` x (64/GS) consecutive sorted occurrences (lane group g of a round holds one
-// occurrence).  A segmented scan across the groups, with a carry between rounds, sums each row's
-// occurrences in order.  A segment that begins and ends inside the piece is applied at its last
-// occurrence.  The piece's first segment, when it began in an earlier piece, is left as a head
-// partial; its last segment, when it runs into the next piece, as a tail partial; k_update_fixup
-// joins them.  Loads are issued a batch of rounds at a time: keys first, then gradient slices
-// together with the state of the rows that end in the batch.
-template <typename RowT, typename GradT>
+// occurrence).  The piece's sorted keys (with one neighbour on each side) and bags are first
+// staged in the wave's LDS region with coalesced loads.  A segmented scan across the groups, with
+// a carry between rounds, then sums each row's occurrences in order.  A segment that begins and
+// ends inside the piece is applied at its last occurrence.  The piece's first segment, when it
+// began in an earlier piece, is left as a head partial; its last segment, when it runs into the
+// next piece, as a tail partial; k_update_fixup joins them.  Each batch of rounds issues its
+// gradient-slice loads together with the state of the rows that end in the batch.
+template <typename RowT, typename GradT, bool VAR, bool MASTER>
 __global__ __launch_bounds__(kBlock) void k_update_pieces(UpdArgs a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   constexpr int BR = SegBatch<EPL>::value;
+  constexpr int kStage = (kPieceMax + 2 + 63) / 64;
   typedef typename F32V<EPL>::t V;
   __shared__ uint32_t s_heads;
+  __shared__ uint32_t s_key[kWaves][kPieceMax + 2];
+  __shared__ uint32_t s_val[kWaves][kPieceMax];
   if (threadIdx.x == 0) s_heads = 0;
   __syncthreads();
   const int GS = 1 << gs_log2;
   const int IPR = 64 >> gs_log2;
   const int PW = a.rounds * IPR;
   const int lane = lane_id();
+  const int wv = threadIdx.x >> 6;
   const int li = lane & (GS - 1);
   const int g = lane >> gs_log2;
   const int e0 = li * EPL;
   const uint32_t NONE = 0xFFFFFFFFu;  // above every row key; equal to the miss key
+  uint32_t* sk = s_key[wv];
+  uint32_t* sv = s_val[wv];
   const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
   uint32_t heads = 0;
   for (int64_t c = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / 64; c < a.n_pieces; c += wstride) {
     const int64_t p0 = c * PW;
     const int64_t p1 = min((int64_t)a.n, p0 + PW);
-    const uint32_t k0 = a.key[p0];
+    // stage keys[p0-1 .. p0+PW] and bags[p0 .. p0+PW) in LDS (clamped reads, then masking)
+    {
+      uint32_t kv[kStage], vv[kStage];
+#pragma unroll
+      for (int q = 0; q < kStage; ++q) {
+        const int64_t idx = p0 - 1 + q * 64 + lane;
+        kv[q] = a.key[min(max(idx, (int64_t)0), (int64_t)a.n - 1)];
+        vv[q] = a.val[min(p0 + q * 64 + lane, (int64_t)a.n - 1)];
+      }
+#pragma unroll
+      for (int q = 0; q < kStage; ++q) {
+        const int j = q * 64 + lane;
+        const int64_t idx = p0 - 1 + j;
+        if (j < PW + 2) sk[j] = (idx >= 0 && idx < a.n) ? kv[q] : NONE;
+        if (j < PW) sv[j] = p0 + j < p1 ? vv[q] : 0u;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const uint32_t k0 = sk[1];
     // the piece's first segment began in an earlier piece
-    const bool cont = k0 < a.miss_key && p0 > 0 && a.key[p0 - 1] == k0;
+    const bool cont = k0 < a.miss_key && sk[0] == k0;
     uint32_t carry_key = NONE;
     V carry = 0.0f;
     int64_t carry_head = -1;
     int carry_D = 0;
     bool head_ended = false;
     for (int rb = 0; rb < a.rounds; rb += BR) {
-      uint32_t k[BR], bag[BR];
-      bool own[BR], hd[BR], upd[BR], cend[BR];
-#pragma unroll
-      for (int r = 0; r < BR; ++r) {
-        const int64_t i = p0 + (int64_t)(rb + r) * IPR + g;
-        const bool valid = i < p1;
-        const uint32_t kk = valid ? a.key[i] : NONE;
-        const uint32_t kp = (valid && i > 0) ? a.key[i - 1] : NONE;
-        const uint32_t kn = (valid && i + 1 < a.n) ? a.key[i + 1] : NONE;
-        own[r] = kk < a.miss_key;
-        k[r] = own[r] ? kk : NONE;
-        hd[r] = own[r] && kp != kk;
-        const bool end = own[r] && kn != kk;
-        const bool is_cont = own[r] && cont && kk == k0;
-        upd[r] = end && !is_cont;
-        cend[r] = end && is_cont;
-        bag[r] = own[r] ? a.val[i] : 0u;
-      }
-      V x[BR];
-      RowState<EPL> st[BR];
+      uint32_t k[BR];
+      bool hd[BR], upd[BR], cend[BR], okg[BR];
+      typename VecOf<GradT, EPL>::t gr[BR];
+      RawState<RowT, EPL, MASTER> st[BR];
       int D[BR];
+      // issue every load of the batch: gradient slices and the state of rows ending here
 #pragma unroll
       for (int r = 0; r < BR; ++r) {
-        D[r] = 0;
-        x[r] = own[r] ? grad_slice<GradT, EPL>(a, bag[r], e0, D[r]) : V(0.0f);
-        upd[r] = upd[r] && e0 < D[r];
-        if (upd[r]) st[r] = load_state<RowT, EPL>(a, k[r], e0);
+        const int j = (rb + r) * IPR + g;
+        const uint32_t kk = sk[j + 1];
+        const uint32_t kp = sk[j];
+        const uint32_t kn = sk[j + 2];
+        const bool own = kk < a.miss_key;
+        k[r] = own ? kk : NONE;
+        hd[r] = own && kp != kk;
+        const bool end = own && kn != kk;
+        const bool is_cont = own && cont && kk == k0;
+        gr[r] = grad_raw<GradT, EPL, VAR>(a, sv[j], e0, own, D[r], okg[r]);
+        upd[r] = end && !is_cont && okg[r];
+        cend[r] = end && is_cont;
+        st[r] = load_state<RowT, EPL, MASTER>(a, k[r], e0, upd[r]);
       }
 #pragma unroll
       for (int r = 0; r < BR; ++r) {
         const int64_t i = p0 + (int64_t)(rb + r) * IPR + g;
         const uint32_t prev_carry = carry_key;
-        const V sum = seg_scan<EPL>(gs_log2, i, k[r], x[r], carry_key, carry, carry_head);
+        const V x = okg[r] ? to_f32<GradT, EPL>(gr[r]) : V(0.0f);
+        const V sum = seg_scan<EPL>(gs_log2, i, k[r], x, carry_key, carry, carry_head);
         if (carry_key != prev_carry) carry_D = __shfl(D[r], (IPR - 1) * GS, 64);
         if (hd[r]) heads += (li == 0);
-        if (upd[r]) apply_state<RowT, EPL>(a, k[r], e0, sum, st[r]);
+        if (upd[r]) apply_state<RowT, EPL, MASTER>(a, k[r], e0, sum, st[r]);
         if (cend[r] && e0 < D[r]) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, sum);
         head_ended = head_ended || (__ballot(cend[r]) != 0);
       }
     }
     // the last segment runs into the next piece: leave its sum for the fixup
     uint32_t flag = head_ended ? (kHeadEnds << 1) : 0u;
-    if (carry_key < a.miss_key && p1 < a.n && a.key[p1] == carry_key) {
+    if (carry_key < a.miss_key && sk[PW + 1] == carry_key) {
       if (cont && carry_key == k0) {
         flag |= kHeadPasses << 1;  // the first segment spans the whole piece
         if (g == 0 && e0 < carry_D) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, carry);
@@ -706,6 +779,8 @@ __global__ __launch_bounds__(kBlock) void k_update_pieces(UpdArgs a, int gs_log2
       }
     }
     if (lane == 0) a.pflag[c] = flag;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
   }
   uint32_t wsum = 0;
   for (int q = 0; q < 64; q += GS) wsum += __shfl(heads, q, 64);
@@ -718,7 +793,7 @@ __global__ __launch_bounds__(kBlock) void k_update_pieces(UpdArgs a, int gs_log2
 // it reads the flags of the following pieces 64 at a time to find where the segment ends, adds the
 // head partials of those pieces in order (lane groups take alternate pieces, then a wave
 // reduction), and applies the update to the row.
-template <typename RowT>
+template <typename RowT, bool MASTER>
 __global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   typedef typename F32V<EPL>::t V;
@@ -735,16 +810,29 @@ __global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2)
     const uint32_t k = a.pkey[2 * t];
     const int D = (int)a.pkey[2 * t + 1];
     const bool on = e0 < D;
-    const RowState<EPL> st = (g == 0 && on) ? load_state<RowT, EPL>(a, k, e0) : RowState<EPL>{};
-    V sum = (g == 0 && on) ? load_f32<float, EPL>(a.ptail + t * a.pdim + e0) : V(0.0f);
+    const bool lead = g == 0 && on;
+    const RawState<RowT, EPL, MASTER> st = load_state<RowT, EPL, MASTER>(a, k, e0, lead);
+    const typename VecOf<float, EPL>::t tail =
+        load_raw<float, EPL>(a.ptail + (lead ? t * a.pdim : 0) + e0);
+    V sum = lead ? to_f32<float, EPL>(tail) : V(0.0f);
     for (int64_t u0 = t + 1; u0 < a.n_pieces; u0 += 64) {
       // pieces u0 .. u0+63: the chain runs through PASS pieces up to the first END piece
       const int64_t u = u0 + lane;
       const uint32_t hk = u < a.n_pieces ? (a.pflag[u] >> 1) & 3u : 0u;
       const uint64_t stop = __ballot(hk != kHeadPasses);
       const int last = stop ? __builtin_ctzll(stop) : 63;  // index of the ending piece
-      for (int q = g; q <= last; q += IPR)
-        if (on && u0 + q < a.n_pieces) sum += load_f32<float, EPL>(a.phead + (u0 + q) * a.pdim + e0);
+      for (int q0 = 0; q0 <= last; q0 += 4 * IPR) {
+        typename VecOf<float, EPL>::t h[4];
+        bool use[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int q = q0 + v * IPR + g;
+          use[v] = on && q <= last && u0 + q < a.n_pieces;
+          h[v] = load_raw<float, EPL>(a.phead + (use[v] ? (u0 + q) * a.pdim : 0) + e0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sum += use[v] ? to_f32<float, EPL>(h[v]) : V(0.0f);
+      }
       if (stop) break;
     }
     // reduce the groups' sums into group 0
@@ -752,7 +840,7 @@ __global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2)
 #pragma unroll
       for (int q = 0; q < EPL; ++q) sum[q] += __shfl_down(sum[q], d * GS, 64);
     }
-    if (g == 0 && on) apply_state<RowT, EPL>(a, k, e0, sum, st);
+    if (lead) apply_state<RowT, EPL, MASTER>(a, k, e0, sum, st);
   }
 }
 
@@ -868,17 +956,16 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
   const int gs = log2_group(a.d.max_dim, a.d.row_f16 ? 8 : 4);
   const dim3 grid((a.n_bags + kFwdBags - 1) / kFwdBags);
   KTimer tm(ctx, "lookup_pool");
+  const dim3 blk(kBlock);
+#define EMB_FWD(R, O, V) hipLaunchKernelGGL((k_lookup_pool<R, O, V>), grid, blk, 0, ctx.stream, a, gs)
   if (a.d.row_f16) {
-    if (a.out_f16)
-      hipLaunchKernelGGL((k_lookup_pool<_Float16, _Float16>), grid, dim3(kBlock), 0, ctx.stream, a, gs);
-    else
-      hipLaunchKernelGGL((k_lookup_pool<_Float16, float>), grid, dim3(kBlock), 0, ctx.stream, a, gs);
+    if (a.out_f16) { if (a.d.var_dim) EMB_FWD(_Float16, _Float16, true); else EMB_FWD(_Float16, _Float16, false); }
+    else { if (a.d.var_dim) EMB_FWD(_Float16, float, true); else EMB_FWD(_Float16, float, false); }
   } else {
-    if (a.out_f16)
-      hipLaunchKernelGGL((k_lookup_pool<float, _Float16>), grid, dim3(kBlock), 0, ctx.stream, a, gs);
-    else
-      hipLaunchKernelGGL((k_lookup_pool<float, float>), grid, dim3(kBlock), 0, ctx.stream, a, gs);
+    if (a.out_f16) { if (a.d.var_dim) EMB_FWD(float, _Float16, true); else EMB_FWD(float, _Float16, false); }
+    else { if (a.d.var_dim) EMB_FWD(float, float, true); else EMB_FWD(float, float, false); }
   }
+#undef EMB_FWD
   return hipGetLastError();
 }
 
@@ -915,7 +1002,8 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
   const int ipr = 64 >> p.gsl;
   const int br = row_f16 ? SegBatch<8>::value : SegBatch<4>::value;
   int64_t r = (nnz + (int64_t)ipr * 131072 - 1) / ((int64_t)ipr * 131072);
-  r = r < br ? br : r > 16 ? 16 : r;
+  const int64_t rmax = kPieceMax / ipr < 16 ? kPieceMax / ipr : 16;
+  r = r < br ? br : r > rmax ? rmax : r;
   p.rounds = (int32_t)((r + br - 1) / br * br);
   const int64_t pw = (int64_t)p.rounds * ipr;
   p.n_pieces = (int32_t)((nnz + pw - 1) / pw);
@@ -1031,18 +1119,30 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   const dim3 gpiece((unsigned)(blocks < 8192 ? blocks : 8192));
   {
     KTimer tm(ctx, "update_pieces");
+#define EMB_UPD(R, G, V, M) hipLaunchKernelGGL((k_update_pieces<R, G, V, M>), gpiece, blk, 0, ctx.stream, u, gsl)
+    const bool var = a.d.var_dim != 0, mst = a.d.has_master != 0;
     if (a.d.row_f16) {
-      if (a.grad_f16) hipLaunchKernelGGL((k_update_pieces<_Float16, _Float16>), gpiece, blk, 0, ctx.stream, u, gsl);
-      else hipLaunchKernelGGL((k_update_pieces<_Float16, float>), gpiece, blk, 0, ctx.stream, u, gsl);
+      if (a.grad_f16) {
+        if (var) { if (mst) EMB_UPD(_Float16, _Float16, true, true); else EMB_UPD(_Float16, _Float16, true, false); }
+        else { if (mst) EMB_UPD(_Float16, _Float16, false, true); else EMB_UPD(_Float16, _Float16, false, false); }
+      } else {
+        if (var) { if (mst) EMB_UPD(_Float16, float, true, true); else EMB_UPD(_Float16, float, true, false); }
+        else { if (mst) EMB_UPD(_Float16, float, false, true); else EMB_UPD(_Float16, float, false, false); }
+      }
     } else {
-      if (a.grad_f16) hipLaunchKernelGGL((k_update_pieces<float, _Float16>), gpiece, blk, 0, ctx.stream, u, gsl);
-      else hipLaunchKernelGGL((k_update_pieces<float, float>), gpiece, blk, 0, ctx.stream, u, gsl);
+      if (a.grad_f16) { if (var) EMB_UPD(float, _Float16, true, false); else EMB_UPD(float, _Float16, false, false); }
+      else { if (var) EMB_UPD(float, float, true, false); else EMB_UPD(float, float, false, false); }
     }
+#undef EMB_UPD
   }
   {
     KTimer tm(ctx, "update_fixup");
-    if (a.d.row_f16) hipLaunchKernelGGL((k_update_fixup<_Float16>), gpiece, blk, 0, ctx.stream, u, gsl);
-    else hipLaunchKernelGGL((k_update_fixup<float>), gpiece, blk, 0, ctx.stream, u, gsl);
+    if (a.d.row_f16) {
+      if (a.d.has_master) hipLaunchKernelGGL((k_update_fixup<_Float16, true>), gpiece, blk, 0, ctx.stream, u, gsl);
+      else hipLaunchKernelGGL((k_update_fixup<_Float16, false>), gpiece, blk, 0, ctx.stream, u, gsl);
+    } else {
+      hipLaunchKernelGGL((k_update_fixup<float, false>), gpiece, blk, 0, ctx.stream, u, gsl);
+    }
   }
   err = hipGetLastError();
   if (err != hipSuccess || !a.unique) return err;
