@@ -124,7 +124,9 @@ struct BwdPlan {
   int32_t rounds;      // rounds per update piece
   int32_t n_pieces;    // update pieces
   int32_t pdim;        // floats per partial
-  size_t off_ka, off_va, off_kb, off_vb, off_counts, off_tot, off_ctr, off_seg;
+  int32_t groups;      // histogram groups of tiles
+  int32_t tile_group;  // tiles per group
+  size_t off_ka, off_va, off_kb, off_vb, off_counts, off_gsum, off_tot, off_ctr, off_seg;
   size_t off_phead, off_ptail, off_pflag, off_pkey;
   size_t bytes;
 };

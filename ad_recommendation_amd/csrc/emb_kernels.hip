@@ -269,8 +269,11 @@ struct SortArgs {
   const uint32_t* vin;
   uint32_t* kout;
   uint32_t* vout;
-  uint32_t* counts;   // [bins][tiles]
+  uint32_t* counts;   // [tiles][bins]: each tile's digit prefix within its group of tiles
+  uint32_t* gsum;     // [groups][bins]: group totals, then their exclusive prefix over groups
   uint32_t* tot;      // [bins]
+  int32_t groups;     // tile groups of tile_group consecutive tiles
+  int32_t tile_group;
   uint32_t* ctr;      // small counters, zeroed by the first scan
   int32_t n;
   int32_t tiles;
@@ -315,67 +318,78 @@ __device__ __forceinline__ int xcd_index(int b, int n) {
   return x * q + min(x, r) + j;
 }
 
-// Per-tile histogram of one digit.  Each thread counts a run of consecutive items and adds runs
-// of equal digits at once (sorted passes hold long runs of one key).  counts is [tile][bin].
+// Digit histograms of a group of tile_group consecutive tiles, one tile after another: each
+// tile's counts are stored as its prefix within the group, and the group's totals apart.  Each
+// thread counts a run of consecutive items and adds runs of equal digits at once (sorted passes
+// hold long runs of one key).  Groups map to XCDs in contiguous ranges.
 template <bool FIRST>
 __global__ __launch_bounds__(kBlock) void k_sort_hist(SortArgs a) {
   __shared__ uint32_t h[kMaxBins];
-  const int t = xcd_index(blockIdx.x, a.tiles);
+  __shared__ uint32_t run[kMaxBins];
+  const int g = xcd_index(blockIdx.x, a.groups);
   const int bins = (1 << a.bits) + 1;
-  for (int d = threadIdx.x; d < bins; d += kBlock) h[d] = 0;
-  __syncthreads();
+  for (int d = threadIdx.x; d < bins; d += kBlock) run[d] = 0;
   const int per = a.tile / kBlock;  // 4, 8 or 16
-  const int32_t i0 = t * a.tile + (int32_t)threadIdx.x * per;
   const uint32_t* src = FIRST ? a.rowref : a.kin;
-  const bool full = (int64_t)(t + 1) * a.tile <= a.n;  // every tile but possibly the last
-  uint32_t k16[16];
-  if (full) {
-    // all of this thread's items first, then the counting
+  const int t1 = min(a.tiles, (g + 1) * a.tile_group);
+  for (int t = g * a.tile_group; t < t1; ++t) {
+    for (int d = threadIdx.x; d < bins; d += kBlock) h[d] = 0;
+    __syncthreads();
+    const int32_t i0 = t * a.tile + (int32_t)threadIdx.x * per;
+    const bool full = (int64_t)(t + 1) * a.tile <= a.n;  // every tile but possibly the last
+    uint32_t k16[16];
+    if (full) {
 #pragma unroll
-    for (int u = 0; u < 16; u += 4) {
-      if (u < per) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + i0 + u);
-        k16[u] = v.x; k16[u + 1] = v.y; k16[u + 2] = v.z; k16[u + 3] = v.w;
+      for (int u = 0; u < 16; u += 4) {
+        if (u < per) {
+          const uint4 v = *reinterpret_cast<const uint4*>(src + i0 + u);
+          k16[u] = v.x; k16[u + 1] = v.y; k16[u + 2] = v.z; k16[u + 3] = v.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) k16[u] = (u < per && i0 + u < a.n) ? src[i0 + u] : 0u;
+    }
+    uint32_t prev = 0xFFFFFFFFu, cnt = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (u < per && i0 + u < a.n) {
+        const uint32_t k = FIRST ? sort_key_of(k16[u], a.rowref_space) : k16[u];
+        const uint32_t dg = digit_of(k, a.shift, a.bits);
+        if (dg != prev) {
+          if (cnt) atomicAdd(&h[prev], cnt);
+          prev = dg;
+          cnt = 0;
+        }
+        ++cnt;
       }
     }
-  } else {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) k16[u] = (u < per && i0 + u < a.n) ? src[i0 + u] : 0u;
-  }
-  uint32_t prev = 0xFFFFFFFFu, run = 0;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    if (u < per && i0 + u < a.n) {
-      const uint32_t k = FIRST ? sort_key_of(k16[u], a.rowref_space) : k16[u];
-      const uint32_t dg = digit_of(k, a.shift, a.bits);
-      if (dg != prev) {
-        if (run) atomicAdd(&h[prev], run);
-        prev = dg;
-        run = 0;
-      }
-      ++run;
+    if (cnt) atomicAdd(&h[prev], cnt);
+    __syncthreads();
+    for (int d = threadIdx.x; d < bins; d += kBlock) {
+      a.counts[(size_t)t * bins + d] = run[d];
+      run[d] += h[d];
     }
   }
-  if (run) atomicAdd(&h[prev], run);
   __syncthreads();
-  for (int d = threadIdx.x; d < bins; d += kBlock) a.counts[(size_t)t * bins + d] = h[d];
+  for (int d = threadIdx.x; d < bins; d += kBlock) a.gsum[(size_t)g * bins + d] = run[d];
 }
 
-// Exclusive scan of each digit's per-tile counts (one block per digit, reading a column of the
-// [tile][bin] matrix; neighbouring digits run on one XCD so they share lines) and digit totals.
+// Exclusive scan over tile groups of each digit's group totals (one block per digit; digits map
+// to XCDs in contiguous ranges so neighbouring digits share lines) and the digit totals.
 __global__ __launch_bounds__(kBlock) void k_sort_scan(SortArgs a, int zero_ctr) {
   __shared__ uint32_t s_w[kWaves];
   const int bins = (1 << a.bits) + 1;
   const int d = xcd_index(blockIdx.x, bins);
   if (zero_ctr && blockIdx.x == 0 && threadIdx.x < 16) a.ctr[threadIdx.x] = 0;
-  uint32_t* col = a.counts + d;
+  uint32_t* col = a.gsum + d;
   uint32_t carry = 0;
-  for (int32_t c0 = 0; c0 < a.tiles; c0 += kBlock * 4) {
+  for (int32_t c0 = 0; c0 < a.groups; c0 += kBlock * 4) {
     uint32_t v[4], s = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int32_t i = c0 + threadIdx.x * 4 + u;
-      v[u] = i < a.tiles ? col[(size_t)i * bins] : 0u;
+      v[u] = i < a.groups ? col[(size_t)i * bins] : 0u;
       s += v[u];
     }
     uint32_t total;
@@ -383,7 +397,7 @@ __global__ __launch_bounds__(kBlock) void k_sort_scan(SortArgs a, int zero_ctr) 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int32_t i = c0 + threadIdx.x * 4 + u;
-      if (i < a.tiles) col[(size_t)i * bins] = pre;
+      if (i < a.groups) col[(size_t)i * bins] = pre;
       pre += v[u];
     }
     carry += total;
@@ -442,7 +456,10 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
 
   // global start of each digit in this tile: all smaller digits, plus this digit in earlier tiles
   block_scan_n<E>(bins, [&](int d) { return a.tot[d]; },
-                  [&](int d, uint32_t v) { s_gbase[d] = v + a.counts[(size_t)t * bins + d]; },
+                  [&](int d, uint32_t v) {
+                    s_gbase[d] = v + a.gsum[(size_t)(t / a.tile_group) * bins + d] +
+                                 a.counts[(size_t)t * bins + d];
+                  },
                   s_w);
   for (int d = tid; d < bins; d += kBlock)
 #pragma unroll
@@ -993,6 +1010,10 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
   p.off_kb = o; o = al(o + 4 * (n + 1));
   p.off_vb = o; o = al(o + 4 * (n + 1));
   p.off_counts = o; o = al(o + 4 * bins * (size_t)(p.tiles > 0 ? p.tiles : 1));
+  // tiles per histogram block: keep at least ~512 blocks, at most 16 tiles each
+  p.tile_group = p.tiles >= 512 * 16 ? 16 : p.tiles >= 512 ? p.tiles / 512 : 1;
+  p.groups = (p.tiles + p.tile_group - 1) / p.tile_group;
+  p.off_gsum = o; o = al(o + 4 * bins * (size_t)(p.groups > 0 ? p.groups : 1));
   p.off_tot = o; o = al(o + 4 * bins);
   p.off_ctr = o; o = al(o + 4 * 16);
   p.off_seg = o; o = al(o + 4 * ((size_t)p.tiles + 1));
@@ -1053,6 +1074,9 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   s.offsets = a.offsets;
   s.n_bags = a.n_bags;
   s.counts = reinterpret_cast<uint32_t*>(ws + p.off_counts);
+  s.gsum = reinterpret_cast<uint32_t*>(ws + p.off_gsum);
+  s.groups = p.groups;
+  s.tile_group = p.tile_group;
   s.tot = reinterpret_cast<uint32_t*>(ws + p.off_tot);
   s.ctr = ctr;
   s.n = p.n;
@@ -1076,8 +1100,8 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
     s.vout = dst_v;
     {
       KTimer tm(ctx, "sort_hist");
-      if (pass == 0) hipLaunchKernelGGL(k_sort_hist<true>, tiles, blk, 0, ctx.stream, s);
-      else hipLaunchKernelGGL(k_sort_hist<false>, tiles, blk, 0, ctx.stream, s);
+      if (pass == 0) hipLaunchKernelGGL(k_sort_hist<true>, dim3(p.groups), blk, 0, ctx.stream, s);
+      else hipLaunchKernelGGL(k_sort_hist<false>, dim3(p.groups), blk, 0, ctx.stream, s);
     }
     {
       KTimer tm(ctx, "sort_scan");

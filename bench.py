@@ -48,7 +48,7 @@ def piece_plan(nnz, max_dim, row_f16):
     ipr = 64 >> gsl
     br = 2 if row_f16 else 4
     r = (nnz + ipr * 131072 - 1) // (ipr * 131072)
-    r = min(max(r, br), 16)
+    r = min(max(r, br), min(16, 256 // ipr))
     rounds = (r + br - 1) // br * br
     return rounds * ipr, (nnz + rounds * ipr - 1) // (rounds * ipr)
 
