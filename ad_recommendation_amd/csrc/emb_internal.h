@@ -76,12 +76,12 @@ struct LaunchCtx {
   Timing* timing;
 };
 
-// Brackets one kernel launch with events when timing is on.
+// Claims a start/stop event pair for one kernel launch when timing is on (r stays null
+// otherwise); the launch records them around the dispatch.
 struct KTimer {
   LaunchCtx& c;
   Timing::Rec* r = nullptr;
   KTimer(LaunchCtx& ctx, const char* name);
-  ~KTimer();
 };
 
 struct FwdLaunch {

@@ -9,10 +9,19 @@
 // to that row only (JD ads article 3.2.1; fp16 rows with fp32 master/state, 3.2.3 and 5.2).
 // Everything is memory-bound: no matrix cores, 16-byte vector loads, LDS for tile staging.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <type_traits>
 
 #include "emb_internal.h"
+
+// Launches a kernel; when the launch is being timed, the dispatch itself carries the start and
+// stop events, so the recorded span is the kernel's own execution, not the gap around it.
+#define EMB_LAUNCH(tm, K, G, B, SHM, ST, ...)                                              \
+  do {                                                                                      \
+    if ((tm).r) hipExtLaunchKernelGGL(K, G, B, SHM, ST, (tm).r->a, (tm).r->b, 0, __VA_ARGS__); \
+    else hipLaunchKernelGGL(K, G, B, SHM, ST, __VA_ARGS__);                                 \
+  } while (0)
 
 namespace emb {
 
@@ -962,10 +971,6 @@ KTimer::KTimer(LaunchCtx& ctx, const char* name) : c(ctx) {
   }
   r = &T.pool[T.used++];
   r->name = name;
-  (void)hipEventRecord(r->a, c.stream);
-}
-KTimer::~KTimer() {
-  if (r) (void)hipEventRecord(r->b, c.stream);
 }
 
 hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
@@ -974,7 +979,7 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
   const dim3 grid((a.n_bags + kFwdBags - 1) / kFwdBags);
   KTimer tm(ctx, "lookup_pool");
   const dim3 blk(kBlock);
-#define EMB_FWD(R, O, V) hipLaunchKernelGGL((k_lookup_pool<R, O, V>), grid, blk, 0, ctx.stream, a, gs)
+#define EMB_FWD(R, O, V) EMB_LAUNCH(tm, (k_lookup_pool<R, O, V>), grid, blk, 0, ctx.stream, a, gs)
   if (a.d.row_f16) {
     if (a.out_f16) { if (a.d.var_dim) EMB_FWD(_Float16, _Float16, true); else EMB_FWD(_Float16, _Float16, false); }
     else { if (a.d.var_dim) EMB_FWD(_Float16, float, true); else EMB_FWD(_Float16, float, false); }
@@ -1039,23 +1044,23 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
 }
 
 template <bool FIRST, int IPT>
-static void launch_scatter_ipt(const SortArgs& s, int logb, dim3 grid, hipStream_t st) {
+static void launch_scatter_ipt(const SortArgs& s, int logb, dim3 grid, hipStream_t st, KTimer& tm) {
   const dim3 blk(kBlock);
   switch (logb) {
-    case 8: hipLaunchKernelGGL((k_sort_scatter<FIRST, IPT, 8>), grid, blk, 0, st, s); break;
-    case 9: hipLaunchKernelGGL((k_sort_scatter<FIRST, IPT, 9>), grid, blk, 0, st, s); break;
-    case 10: hipLaunchKernelGGL((k_sort_scatter<FIRST, IPT, 10>), grid, blk, 0, st, s); break;
-    default: hipLaunchKernelGGL((k_sort_scatter<FIRST, IPT, 11>), grid, blk, 0, st, s); break;
+    case 8: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 8>), grid, blk, 0, st, s); break;
+    case 9: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 9>), grid, blk, 0, st, s); break;
+    case 10: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 10>), grid, blk, 0, st, s); break;
+    default: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 11>), grid, blk, 0, st, s); break;
   }
 }
 
 template <bool FIRST>
-static void launch_scatter(const SortArgs& s, int ipt, int logb, dim3 grid, hipStream_t st) {
+static void launch_scatter(const SortArgs& s, int ipt, int logb, dim3 grid, hipStream_t st, KTimer& tm) {
   switch (ipt) {
-    case 2: launch_scatter_ipt<FIRST, 2>(s, logb, grid, st); break;
-    case 4: launch_scatter_ipt<FIRST, 4>(s, logb, grid, st); break;
-    case 8: launch_scatter_ipt<FIRST, 8>(s, logb, grid, st); break;
-    default: launch_scatter_ipt<FIRST, 16>(s, logb, grid, st); break;
+    case 2: launch_scatter_ipt<FIRST, 2>(s, logb, grid, st, tm); break;
+    case 4: launch_scatter_ipt<FIRST, 4>(s, logb, grid, st, tm); break;
+    case 8: launch_scatter_ipt<FIRST, 8>(s, logb, grid, st, tm); break;
+    default: launch_scatter_ipt<FIRST, 16>(s, logb, grid, st, tm); break;
   }
 }
 
@@ -1065,7 +1070,7 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   if (p.n <= 0) {
     if (a.n_unique) {
       KTimer tm(ctx, "set_n_unique");
-      hipLaunchKernelGGL(k_set_i64, dim3(1), dim3(1), 0, ctx.stream, a.n_unique, (int64_t)0);
+      EMB_LAUNCH(tm, k_set_i64, dim3(1), dim3(1), 0, ctx.stream, a.n_unique, (int64_t)0);
     }
     return hipGetLastError();
   }
@@ -1100,17 +1105,17 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
     s.vout = dst_v;
     {
       KTimer tm(ctx, "sort_hist");
-      if (pass == 0) hipLaunchKernelGGL(k_sort_hist<true>, dim3(p.groups), blk, 0, ctx.stream, s);
-      else hipLaunchKernelGGL(k_sort_hist<false>, dim3(p.groups), blk, 0, ctx.stream, s);
+      if (pass == 0) EMB_LAUNCH(tm, k_sort_hist<true>, dim3(p.groups), blk, 0, ctx.stream, s);
+      else EMB_LAUNCH(tm, k_sort_hist<false>, dim3(p.groups), blk, 0, ctx.stream, s);
     }
     {
       KTimer tm(ctx, "sort_scan");
-      hipLaunchKernelGGL(k_sort_scan, nbins, blk, 0, ctx.stream, s, pass == 0 ? 1 : 0);
+      EMB_LAUNCH(tm, k_sort_scan, nbins, blk, 0, ctx.stream, s, pass == 0 ? 1 : 0);
     }
     {
       KTimer tm(ctx, "sort_scatter");
-      if (pass == 0) launch_scatter<true>(s, p.ipt, logb, tiles, ctx.stream);
-      else launch_scatter<false>(s, p.ipt, logb, tiles, ctx.stream);
+      if (pass == 0) launch_scatter<true>(s, p.ipt, logb, tiles, ctx.stream, tm);
+      else launch_scatter<false>(s, p.ipt, logb, tiles, ctx.stream, tm);
     }
     src_k = dst_k;
     src_v = dst_v;
@@ -1143,7 +1148,7 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   const dim3 gpiece((unsigned)(blocks < 8192 ? blocks : 8192));
   {
     KTimer tm(ctx, "update_pieces");
-#define EMB_UPD(R, G, V, M) hipLaunchKernelGGL((k_update_pieces<R, G, V, M>), gpiece, blk, 0, ctx.stream, u, gsl)
+#define EMB_UPD(R, G, V, M) EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M>), gpiece, blk, 0, ctx.stream, u, gsl)
     const bool var = a.d.var_dim != 0, mst = a.d.has_master != 0;
     if (a.d.row_f16) {
       if (a.grad_f16) {
@@ -1162,10 +1167,10 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   {
     KTimer tm(ctx, "update_fixup");
     if (a.d.row_f16) {
-      if (a.d.has_master) hipLaunchKernelGGL((k_update_fixup<_Float16, true>), gpiece, blk, 0, ctx.stream, u, gsl);
-      else hipLaunchKernelGGL((k_update_fixup<_Float16, false>), gpiece, blk, 0, ctx.stream, u, gsl);
+      if (a.d.has_master) EMB_LAUNCH(tm, (k_update_fixup<_Float16, true>), gpiece, blk, 0, ctx.stream, u, gsl);
+      else EMB_LAUNCH(tm, (k_update_fixup<_Float16, false>), gpiece, blk, 0, ctx.stream, u, gsl);
     } else {
-      hipLaunchKernelGGL((k_update_fixup<float, false>), gpiece, blk, 0, ctx.stream, u, gsl);
+      EMB_LAUNCH(tm, (k_update_fixup<float, false>), gpiece, blk, 0, ctx.stream, u, gsl);
     }
   }
   err = hipGetLastError();
@@ -1184,23 +1189,23 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   g.nvalid = ctr + 2;
   {
     KTimer tm(ctx, "seg_zero");
-    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, ctx.stream, ctr + 2, 1);
+    EMB_LAUNCH(tm, k_zero_words, dim3(1), dim3(64), 0, ctx.stream, ctr + 2, 1);
   }
   {
     KTimer tm(ctx, "seg_count");
-    hipLaunchKernelGGL(k_seg_count, tiles, blk, 0, ctx.stream, g);
+    EMB_LAUNCH(tm, k_seg_count, tiles, blk, 0, ctx.stream, g);
   }
   {
     KTimer tm(ctx, "seg_scan");
-    hipLaunchKernelGGL(k_seg_scan, dim3(1), blk, 0, ctx.stream, g);
+    EMB_LAUNCH(tm, k_seg_scan, dim3(1), blk, 0, ctx.stream, g);
   }
   {
     KTimer tm(ctx, "seg_write");
-    hipLaunchKernelGGL(k_seg_write, tiles, blk, 0, ctx.stream, g);
+    EMB_LAUNCH(tm, k_seg_write, tiles, blk, 0, ctx.stream, g);
   }
   if (a.count) {
     KTimer tm(ctx, "seg_counts");
-    hipLaunchKernelGGL(k_seg_counts, dim3(1024), blk, 0, ctx.stream, g);
+    EMB_LAUNCH(tm, k_seg_counts, dim3(1024), blk, 0, ctx.stream, g);
   }
   return hipGetLastError();
 }

@@ -90,7 +90,7 @@ def sort_plan(nnz, rowref_space):
     return ipt, (nnz + 256 * ipt - 1) // (256 * ipt), bits
 
 
-def kernel_bytes(name, st, w, passes):
+def kernel_bytes(name, st, w, rowref_space):
     """Algorithmic bytes one launch of `name` moves for a batch with stats `st`: every datum the
     kernel must read or write once (no cache reuse), as in the design's byte model."""
     sr = 2 if w.row_dtype == "f16" else 4
@@ -102,13 +102,16 @@ def kernel_bytes(name, st, w, passes):
     if name == "lookup_pool":
         # key in, slot hit (key compare + row prefix), row gather, rowref out; offsets, pooled out
         return n * (8 + 12 + 4) + st["occ_elems"] * sr + st["bags"] * 4 + st["bag_elems"] * so
-    if name == "sort_hist":
-        return n * 4
-    if name == "sort_scan":
-        ipt, tiles, bits = sort_plan(n, passes)
-        return ((1 << bits) + 1) * tiles * 8
-    if name == "sort_scatter":
-        return n * 16 / 1.0
+    if name in ("sort_hist", "sort_scan", "sort_scatter"):
+        ipt, tiles, bits = sort_plan(n, rowref_space)
+        bins = (1 << bits) + 1                          # digits plus the miss bin
+        tile_group = 16 if tiles >= 512 * 16 else tiles // 512 if tiles >= 512 else 1
+        groups = (tiles + tile_group - 1) // tile_group
+        if name == "sort_hist":                         # keys in; per-tile and per-group counts out
+            return n * 4 + (tiles + groups) * bins * 4
+        if name == "sort_scan":                         # group totals scanned in place
+            return groups * bins * 8
+        return n * 16 + (tiles + groups) * bins * 4     # pairs in and out; counts in
     if name == "update_pieces":
         # every occurrence's sorted pair and gradient slice; rows finished inside a piece;
         # head/tail partials of pieces whose segments cross
@@ -134,8 +137,9 @@ def load_traffic(workload, kernel):
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline_child(name: str, max_seconds: float):
-    """Time the oracle's forward + backward on batch 0 of the workload (one thread)."""
+def cpu_baseline_child(name: str, min_seconds: float, max_batches: int):
+    """Time the oracle's forward + backward (one thread) on consecutive batches of the workload,
+    from batch 0, until at least min_seconds of oracle work or max_batches batches are done."""
     from gen import synth, workloads as W
     from oracle import emb_oracle as O
     w = W.get(name)
@@ -146,12 +150,19 @@ def cpu_baseline_child(name: str, max_seconds: float):
     ot = O.Table(keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor, w.acc_init, rows,
                  master=master)
     build_s = time.perf_counter() - t0
-    bt = synth.batch(w, 0)
-    t0 = time.perf_counter()
-    ot.forward(bt["keys"], bt["offsets"], w.out_dtype)
-    t_fwd = time.perf_counter() - t0
-    u, _, _, _ = ot.backward(bt["keys"], bt["offsets"], bt["grad"], w.lr, w.eps)
-    t = time.perf_counter() - t0
+    t = t_fwd = 0.0
+    nnz = n_u = nb = 0
+    while nb < max_batches and t < min_seconds:
+        bt = synth.batch(w, nb)
+        t0 = time.perf_counter()
+        ot.forward(bt["keys"], bt["offsets"], w.out_dtype)
+        t1 = time.perf_counter()
+        u, _, _, _ = ot.backward(bt["keys"], bt["offsets"], bt["grad"], w.lr, w.eps)
+        t += time.perf_counter() - t0
+        t_fwd += t1 - t0
+        nnz += int(bt["keys"].size)
+        n_u += int(u.size)
+        nb += 1
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -161,14 +172,14 @@ def cpu_baseline_child(name: str, max_seconds: float):
     except OSError:
         pass
     print(json.dumps({"seconds": t, "fwd_seconds": t_fwd, "build_seconds": build_s,
-                      "nnz": int(bt["keys"].size), "U": int(u.size), "cpu": cpu,
+                      "batches": nb, "nnz": nnz, "U": n_u, "cpu": cpu,
                       "nproc": os.cpu_count()}))
 
 
 def run_cpu_baseline(name: str):
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
     code = ("import os,sys; os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]}); "
-            f"sys.path.insert(0, {ROOT!r}); import bench; bench.cpu_baseline_child({name!r}, 60)")
+            f"sys.path.insert(0, {ROOT!r}); import bench; bench.cpu_baseline_child({name!r}, 12.0, 64)")
     r = subprocess.run([sys.executable, "-c", code], env=env, stdout=subprocess.PIPE,
                        stderr=subprocess.PIPE, text=True, timeout=900)
     if r.returncode != 0:
@@ -186,6 +197,8 @@ def main():
     ap.add_argument("--workload", default="f26")
     ap.add_argument("--ring", type=int, default=0, help="distinct batches cycled (0 = workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES, five times (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         sys.exit("bench.py measures one GPU: this build has no multi-GPU path (the sharded design "
@@ -198,6 +211,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration}), flush=True)
+        return
     w = W.get(args.workload)
     R = args.ring or min(w.ring, 16)
     dims = synth.field_dims(w)
@@ -206,13 +227,31 @@ def main():
     rows, master = synth.initial_state(w)
     log(f"[bench] {w.name}: {keys.size} keys generated in {time.perf_counter() - t0:.1f}s")
     t0 = time.perf_counter()
-    T = emb.Table(dims, emb.EMB_F16 if w.row_dtype == "f16" else emb.EMB_F32, w.has_master,
-                  w.n_tables, w.load_factor, w.acc_init, keys, rows, None, master)
+    rdt = emb.EMB_F16 if w.row_dtype == "f16" else emb.EMB_F32
+    try:  # pinned host image: the PASS flash is one DMA from page-locked memory
+        T = emb.Table(dims, rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init, keys, rows,
+                      None, master, flags=emb.FLAG_PINNED_STAGING)
+        pinned = True
+    except emb.EmbError as e:
+        log(f"[bench] pinned host image unavailable ({e}); using pageable memory")
+        T = emb.Table(dims, rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init, keys, rows,
+                      None, master)
+        pinned = False
     del rows, master
     log(f"[bench] table built in {time.perf_counter() - t0:.1f}s; arena "
         f"{T.info['arena_bytes'] / 2**30:.2f} GiB")
-    T.flash(dev)
-    torch.cuda.synchronize()
+    T.arena = torch.empty(emb.table_device_bytes(T.h), dtype=torch.uint8, device=dev)
+    flash_ms = []
+    for _ in range(2):  # the PASS flash (host image -> HBM), timed on its own
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        T.flash(dev)
+        torch.cuda.synchronize()
+        flash_ms.append((time.perf_counter() - f0) * 1e3)
+    flash = {"bytes": int(T.info["arena_bytes"]), "ms": min(flash_ms), "pinned": pinned,
+             "GB_per_s": T.info["arena_bytes"] / (min(flash_ms) / 1e3) / 1e9}
+    log(f"[bench] pass_flash: {flash['bytes'] / 1e9:.2f} GB in {flash['ms']:.1f} ms "
+        f"({flash['GB_per_s']:.1f} GB/s, pinned={pinned})")
 
     odt = torch.float16 if w.out_dtype == "f16" else torch.float32
     out_code = emb.EMB_F16 if w.out_dtype == "f16" else emb.EMB_F32
@@ -235,7 +274,7 @@ def main():
         ws_bytes = max(ws_bytes, emb.bwd_workspace_bytes(T.h, n_bags, st["nnz"]))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     n_unique = torch.zeros(R, dtype=torch.int64, device=dev)
-    passes = T.info["rowref_space"]
+    rowref_space = T.info["rowref_space"]
     log(f"[bench] ring of {R} batches staged; mean nnz {np.mean([r['nnz'] for r in ring]):.0f}, "
         f"mean unique {np.mean([r['st']['U'] for r in ring]):.0f}")
 
@@ -256,7 +295,14 @@ def main():
     torch.cuda.synchronize()
     calib = emb.emb_timing_read(T.h)
     per_step = {k: v[1] / R for k, v in calib.items()}
-    dominant = max(per_step, key=per_step.get)
+    # the dominant kernel: longest per launch (the sort's passes are separate launches)
+    dominant = max(calib, key=lambda k: calib[k][1] / max(calib[k][0], 1))
+    kernels = {}
+    for k, (cnt, kms) in calib.items():
+        b = np.mean([kernel_bytes(k, r["st"], w, rowref_space) for r in ring]) * cnt / R
+        kernels[k] = {"launches_per_step": cnt / R, "ms_per_step": kms / R,
+                      "alg_bytes_per_step": float(b), "GB_per_s": float(b / (kms / R) / 1e6)}
+    alg_step = sum(v["alg_bytes_per_step"] for v in kernels.values())
     log("[bench] per-step kernel time (ms): " +
         ", ".join(f"{k} {v:.4f}" for k, v in sorted(per_step.items(), key=lambda x: -x[1])))
     got_u = n_unique.cpu().numpy()
@@ -282,7 +328,7 @@ def main():
     value = rows_done / (ms / 1e3)
     # algorithmic bytes of the dominant kernel over its timed launches
     per_step_launches = dom[0] / args.steps
-    dom_bytes = sum(kernel_bytes(dominant, ring[i % R]["st"], w, passes) for i in range(args.steps))
+    dom_bytes = sum(kernel_bytes(dominant, ring[i % R]["st"], w, rowref_space) for i in range(args.steps))
     dom_bytes *= per_step_launches
     achieved = dom_bytes / (dom[1] / 1e3) / 1e9
     traffic = load_traffic(w.name, dominant)
@@ -293,10 +339,10 @@ def main():
         if c:
             cpu = {"value": (c["nnz"] + c["U"]) / c["seconds"], "unit": "rows/s", "cores": 1,
                    "kind": "oracle",
-                   "sample": f"one full batch (batch 0: {c['nnz']} lookups, {c['U']} rows updated) "
-                             f"of {w.name}, oracle forward+backward, 1 thread on {c['cpu']} "
-                             f"({c['nproc']} cpus visible); table build {c['build_seconds']:.1f}s "
-                             f"excluded; {c['seconds']:.2f}s"}
+                   "sample": f"batches 0..{c['batches'] - 1} of {w.name} ({c['nnz']} lookups, "
+                             f"{c['U']} row updates), oracle forward+backward in sequence, "
+                             f"1 thread on {c['cpu']} ({c['nproc']} cpus visible); table build "
+                             f"{c['build_seconds']:.1f}s excluded; {c['seconds']:.2f}s timed"}
     res = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms / args.steps, "higher_is_better": True,
@@ -315,7 +361,11 @@ def main():
                      "avg_launch_ms": dom[1] / max(dom[0], 1),
                      "alg_bytes_per_launch": dom_bytes / max(dom[0], 1)},
         "cpu_baseline": cpu,
-        "kernel_ms_per_step": per_step,
+        "pass_flash": flash,
+        "step_hbm": {"alg_bytes_per_step": alg_step,
+                     "GB_per_s": alg_step / (ms / args.steps) / 1e6,
+                     "frac": alg_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS},
+        "kernels": kernels,
     }
     print(json.dumps(res), flush=True)
 
