@@ -197,6 +197,7 @@ struct EmbTable {
   bool pinned = false;
   std::vector<uint64_t> row_keys;  // keys in rowref order
   std::vector<uint32_t> row_ref;   // their rowrefs (ascending)
+  std::vector<uint32_t> row_of_key;  // position in row_keys of the i-th key given at create
   double mean_disp = 0;
   uint64_t max_disp = 0;
   // device
@@ -355,10 +356,17 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
   if (bad.load() == 1) return fail(EMB_ESENTINEL, "a key equals the EMPTY marker (all bits set)");
   if (bad.load() == 2) return fail(EMB_ERANGE, "a key's field id is >= n_fields");
 
-  // input row offsets (elements) in key order
-  std::vector<uint64_t> in_off(N + 1, 0);
-  for (size_t i = 0; i < N; ++i) in_off[i + 1] = in_off[i] + (uint64_t)T->dim[(int)(K[i] >> 48)];
-  T->total_elems = in_off[N];
+  // input row offsets (elements) in key order; implicit (i * D) when every field has width D
+  std::vector<uint64_t> in_off;
+  if (T->var_dim) {
+    in_off.assign(N + 1, 0);
+    for (size_t i = 0; i < N; ++i) in_off[i + 1] = in_off[i] + (uint64_t)T->dim[(int)(K[i] >> 48)];
+    T->total_elems = in_off[N];
+  } else {
+    T->total_elems = (uint64_t)N * (uint64_t)T->dim[0];
+  }
+  const uint64_t fixed_d = (uint64_t)T->dim[0];
+  auto src_off = [&](size_t i) { return T->var_dim ? in_off[i] : (uint64_t)i * fixed_d; };
 
   // per table: homes, sort by (home, key), place, count buckets
   std::vector<Entry> ent[2];
@@ -459,7 +467,13 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
       run += (uint64_t)T->gran[(int)(E[i].key >> 48)];
     }
     for (; next_b < s.n_buckets; ++next_b) kb[next_b * kWordsPerBucket + 15] = run;
+    std::vector<Entry>().swap(ent[t]);
+    std::vector<uint64_t>().swap(slot_of[t]);
   }
+  T->row_of_key.resize(N);
+  parallel_for(N, [&](size_t b, size_t e) {
+    for (size_t r = b; r < e; ++r) T->row_of_key[idx_by_row[r]] = (uint32_t)r;
+  });
 
   // rows, accumulator, master in rowref order
   uint8_t* R = T->image + T->off_rows;
@@ -470,9 +484,9 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
   parallel_for(N, [&](size_t b, size_t e) {
     for (size_t r = b; r < e; ++r) {
       const uint32_t i = idx_by_row[r];
-      const uint64_t D = in_off[i + 1] - in_off[i];
+      const uint64_t D = (uint64_t)T->dim[(int)(T->row_keys[r] >> 48)];
       const uint64_t dst = (uint64_t)T->row_ref[r] * (uint64_t)T->granule;
-      const uint64_t src = in_off[i];
+      const uint64_t src = src_off(i);
       if (rin) {
         std::memcpy(R + dst * eb, rin + src * eb, D * eb);
       } else if (master && f16rows) {
@@ -650,6 +664,53 @@ int table_export(const EmbTable* t, const int64_t* keys, int64_t n, void* rows, 
     if (master) std::memcpy(master + o, reinterpret_cast<const float*>(t->image + t->off_master) + e, D * 4);
     o += D;
   }
+  return EMB_OK;
+}
+
+int table_fill_state(EmbTable* t, int64_t first, int64_t n, const void* rows, const float* acc,
+                     const float* master) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  if (first < 0 || n < 0 || (uint64_t)first + (uint64_t)n > t->n_keys)
+    return fail(EMB_EINVAL, "table_fill_state: key range outside the key list given at create");
+  if (master && !t->has_master) return fail(EMB_EINVAL, "table keeps no master copy");
+  if (n == 0 || (!rows && !acc && !master)) return EMB_OK;
+  const size_t eb = t->elem_bytes;
+  const bool f16 = t->row_dtype == EMB_F16;
+  // element offset of each key's slice inside the caller's packed arrays
+  std::vector<uint64_t> off;
+  if (t->var_dim) {
+    off.resize((size_t)n + 1, 0);
+    for (int64_t i = 0; i < n; ++i) {
+      const uint64_t k = t->row_keys[t->row_of_key[(size_t)(first + i)]];
+      off[(size_t)i + 1] = off[(size_t)i] + (uint64_t)t->dim[(int)(k >> 48)];
+    }
+  }
+  uint8_t* R = t->image + t->off_rows;
+  float* A = reinterpret_cast<float*>(t->image + t->off_acc);
+  float* M = t->has_master ? reinterpret_cast<float*>(t->image + t->off_master) : nullptr;
+  parallel_for((size_t)n, [&](size_t b, size_t e) {
+    for (size_t i = b; i < e; ++i) {
+      const uint32_t r = t->row_of_key[(size_t)first + i];
+      const uint64_t D = (uint64_t)t->dim[(int)(t->row_keys[r] >> 48)];
+      const uint64_t src = t->var_dim ? off[i] : (uint64_t)i * D;
+      const uint64_t dst = (uint64_t)t->row_ref[r] * (uint64_t)t->granule;
+      if (rows) {
+        std::memcpy(R + dst * eb, static_cast<const uint8_t*>(rows) + src * eb, D * eb);
+      } else if (master && f16) {
+        uint16_t* h = reinterpret_cast<uint16_t*>(R) + dst;
+        for (uint64_t q = 0; q < D; ++q) h[q] = f32_to_f16(master[src + q]);
+      }
+      if (acc) std::memcpy(A + dst, acc + src, D * 4);
+      if (M) {
+        if (master) {
+          std::memcpy(M + dst, master + src, D * 4);
+        } else if (rows) {
+          const uint16_t* h = reinterpret_cast<const uint16_t*>(R) + dst;
+          for (uint64_t q = 0; q < D; ++q) M[dst + q] = f16_to_f32(h[q]);
+        }
+      }
+    }
+  });
   return EMB_OK;
 }
 

@@ -68,6 +68,7 @@ def lib() -> C.CDLL:
                                C.c_size_t, _VP, _VP, _VP, _VP],
         "pass_writeback": [_VP, _VP],
         "table_export": [_VP, _VP, _I64, _VP, _VP, _VP],
+        "table_fill_state": [_VP, _I64, _I64, _VP, _VP, _VP],
         "table_key_rowref": [_VP, _VP, _I64, _VP, _VP],
         "table_rowref_keys": [_VP, _VP, _I64, _VP],
         "emb_timing_enable": [_VP, C.c_int, C.c_char_p],
@@ -89,7 +90,7 @@ def exported_symbols():
     """Names include/emb.h declares (used by the load test)."""
     return ["table_create_from_prebuilt", "table_info", "table_device_bytes", "pass_flash",
             "lookup_pool_fwd", "bwd_workspace_bytes", "sparse_adagrad_bwd", "pass_writeback",
-            "table_export", "table_key_rowref", "table_rowref_keys", "emb_timing_enable",
+            "table_export", "table_fill_state", "table_key_rowref", "table_rowref_keys", "emb_timing_enable",
             "emb_timing_read", "table_destroy", "emb_last_error"]
 
 
@@ -212,6 +213,16 @@ def table_export(h, keys, width: int, row_dtype: int, want_master: bool):
     return rows, acc, master
 
 
+def table_fill_state(h, first: int, n: int, row_dtype: int, rows=None, acc=None, master=None):
+    """Write rows / acc / master of keys [first, first+n) of the create-time key list into the
+    host image (packed in that list's order); takes effect at the next flash."""
+    rdt = np.float16 if row_dtype == EMB_F16 else np.float32
+    rows = None if rows is None else _host(np.asarray(rows), rdt)
+    acc = None if acc is None else _host(np.asarray(acc), np.float32)
+    master = None if master is None else _host(np.asarray(master), np.float32)
+    _check(lib().table_fill_state(h, int(first), int(n), _hp(rows), _hp(acc), _hp(master)))
+
+
 def table_key_rowref(h, keys):
     keys = _host(np.asarray(keys).view(np.int64), np.int64)
     rr = np.empty(keys.size, dtype=np.uint32)
@@ -276,6 +287,9 @@ class Table:
         if self.arena is None:
             self.arena = torch.empty(table_device_bytes(self.h), dtype=torch.uint8, device=device)
         pass_flash(self.h, self.arena, stream)
+
+    def fill_state(self, first: int, n: int, rows=None, acc=None, master=None):
+        table_fill_state(self.h, first, n, self.row_dtype, rows, acc, master)
 
     def export(self, keys):
         k = np.asarray(keys).view(np.uint64)

@@ -21,6 +21,8 @@ Input shapes follow the pages:
 from __future__ import annotations
 
 import functools
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -88,9 +90,33 @@ def field_keys(w: Workload, f: int) -> np.ndarray:
     return compose(np.full(n_f, fid, dtype=np.uint64), raw)
 
 
+def worker_count() -> int:
+    """Threads for per-field generation (numpy releases the GIL inside bulk draws and sorts)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def per_field(w: Workload, fn):
+    """[fn(f) for every field], fields drawn in parallel when the workload is large.  Every field
+    has its own stream, so the result does not depend on the thread count."""
+    if w.n_keys < (1 << 24) or worker_count() == 1:
+        return [fn(f) for f in range(w.n_fields)]
+    with ThreadPoolExecutor(worker_count()) as ex:
+        return list(ex.map(fn, range(w.n_fields)))
+
+
 @functools.lru_cache(maxsize=4)
 def _resident_keys_cached(w: Workload) -> np.ndarray:
-    return np.concatenate([field_keys(w, f) for f in range(w.n_fields)])
+    parts = per_field(w, lambda f: field_keys(w, f))
+    out = np.empty(w.n_keys, dtype=np.uint64)
+    o = 0
+    for p in parts:
+        out[o:o + p.size] = p
+        o += p.size
+    return out
 
 
 def resident_keys(w: Workload) -> np.ndarray:
@@ -106,30 +132,27 @@ def field_key_offsets(w: Workload) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------- rows / state
-def initial_state(w: Workload):
-    """Initial rows (packed in key order, width D of the key's field) and the fp32
+def field_state(w: Workload, f: int):
+    """Initial rows of field f's keys (packed in key order, D_f elements each) and their fp32
     master copy when the workload keeps one.
 
-    Rows are N(0, row_std) drawn in fp32.  fp16 rows are the round-to-nearest
-    fp16 of that draw, and the draw itself is the master copy.
-    Returns (rows, master_or_None); the Adagrad accumulator starts at
-    ``w.acc_init`` and is not materialised here."""
-    dims = field_dims(w)
-    counts = field_key_counts(w)
-    parts_r: List[np.ndarray] = []
-    parts_m: List[np.ndarray] = []
-    for f in range(w.n_fields):
-        r = rng_for(w, S_ROWS, f)
-        draw = (r.standard_normal(int(counts[f]) * int(dims[f]), dtype=np.float32)
-                * np.float32(w.row_std))
-        if w.row_dtype == "f32":
-            parts_r.append(draw)
-        else:
-            parts_r.append(draw.astype(np.float16))
-            if w.has_master:
-                parts_m.append(draw)
-    rows = np.concatenate(parts_r)
-    master = np.concatenate(parts_m) if parts_m else None
+    Rows are N(0, row_std) drawn in fp32 from the field's own stream.  fp16 rows are the
+    round-to-nearest fp16 of that draw, and the draw itself is the master copy.
+    Returns (rows_f, master_f_or_None)."""
+    n = int(field_key_counts(w)[f]) * int(field_dims(w)[f])
+    draw = rng_for(w, S_ROWS, f).standard_normal(n, dtype=np.float32) * np.float32(w.row_std)
+    if w.row_dtype == "f32":
+        return draw, None
+    return draw.astype(np.float16), (draw if w.has_master else None)
+
+
+def initial_state(w: Workload):
+    """Initial rows of every resident key (packed in key order, width D of the key's field) and
+    the fp32 master copy when the workload keeps one: the fields' ``field_state`` in field order.
+    The Adagrad accumulator starts at ``w.acc_init`` and is not materialised here."""
+    parts = [field_state(w, f) for f in range(w.n_fields)]
+    rows = np.concatenate([p[0] for p in parts])
+    master = np.concatenate([p[1] for p in parts]) if w.has_master else None
     return rows, master
 
 
@@ -165,7 +188,12 @@ def zipf_ranks(r: np.random.Generator, n_draw: int, n_items: int, alpha: float) 
     truncated law, equivalent to rejecting draws above n_items)."""
     cdf = _zipf_cdf(int(n_items), float(alpha))
     u = r.random(n_draw)
-    return np.minimum(np.searchsorted(cdf, u, side="right"), n_items - 1) + 1
+    # search in ascending order of u (each search starts where the previous one ended), then put
+    # the results back in draw order
+    order = np.argsort(u, kind="stable")
+    idx = np.empty(n_draw, dtype=np.int64)
+    idx[order] = np.searchsorted(cdf, u[order], side="right")
+    return np.minimum(idx, n_items - 1) + 1
 
 
 def _longtail_occurrences(r: np.random.Generator, n_f: int, n_items: int, alpha: float):

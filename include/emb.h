@@ -178,6 +178,23 @@ int pass_writeback(EmbTable* t, emb_stream_t stream);
 int table_export(const EmbTable* t, const int64_t* keys, int64_t n, void* rows, float* acc,
                  float* master);
 
+/*
+ * Write rows and state into the host image for keys [first, first + n) of the key list given to
+ * table_create_from_prebuilt, in that list's order: rows (row_dtype), acc and master (fp32) are
+ * packed like the create arrays, each key with the width of its field.  Lets a caller stream a
+ * PASS's state into the image in pieces (create with rows, acc and master NULL, then fill) instead
+ * of holding it twice (Tencent PCG GPU training talk, flash paragraph: the whole table is prepared
+ * off the GPU and then copied in one piece).
+ *   rows NULL with master given (fp16 table): rows become the fp16 round-to-nearest of master.
+ *   master NULL on a table with a master copy: master becomes f32(row) when rows are given.
+ *   acc NULL: the accumulator is left as it is (acc_init after create).
+ * Host only; it takes effect at the next pass_flash, and must not run while a pass_flash or
+ * pass_writeback copy of this table is in flight.  A range outside the key list, or master on a
+ * table without one, gives EMB_EINVAL.
+ */
+int table_fill_state(EmbTable* t, int64_t first, int64_t n, const void* rows, const float* acc,
+                     const float* master);
+
 /* Host-side lookup of n keys: rowref (EMB_ROWREF_MISS if absent) and logical slot (-1). */
 int table_key_rowref(const EmbTable* t, const int64_t* keys, int64_t n, uint32_t* rowref,
                      int64_t* slot);

@@ -162,3 +162,49 @@ def test_workspace_size_grows_with_batch():
     a = emb.bwd_workspace_bytes(T.h, 256, 1024)
     b = emb.bwd_workspace_bytes(T.h, 256 * 64, 1024 * 64)
     assert 0 < a < b and b >= 16 * 1024 * 64
+
+
+@pytest.mark.parametrize("w", [W.scaled(W.F26, n_keys=120_000, batch=16),
+                               W.scaled(W.F40_VARDIM, n_keys=160_000, batch=16),
+                               W.scaled(W.F100, n_keys=90_000, batch=16)])
+def test_fill_state_in_pieces_equals_create_with_state(w):
+    """Streaming a PASS's state into the image field by field gives the same image as handing it
+    all over at create."""
+    T_all, keys, rows, master = _table(w)
+    rdt = emb.EMB_F16 if w.row_dtype == "f16" else emb.EMB_F32
+    T = emb.Table(synth.field_dims(w), rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init,
+                  keys)
+    foff = synth.field_key_offsets(w)
+    acc_all = np.full(rows.size, 0.25, dtype=np.float32)
+    roff = synth.row_offsets(w)
+    for f in range(w.n_fields):
+        r_f, m_f = synth.field_state(w, f)
+        a, b = int(foff[f]), int(foff[f + 1])
+        if w.has_master and f % 2:        # odd fields: rows derived from the master copy
+            T.fill_state(a, b - a, None, acc_all[roff[a]:roff[b]], m_f)
+        else:
+            T.fill_state(a, b - a, r_f, acc_all[roff[a]:roff[b]], m_f)
+    r1, a1, m1 = T_all.export(keys)
+    r2, a2, m2 = T.export(keys)
+    assert np.array_equal(r1.view(np.uint8), r2.view(np.uint8))
+    assert np.all(a2 == 0.25)
+    if w.has_master:
+        assert np.array_equal(m1.view(np.uint32), m2.view(np.uint32))
+
+
+def test_fill_state_errors():
+    w = W.scaled(W.F100, n_keys=20_000, batch=4)
+    T_all, keys, rows, master = _table(w)
+    T = emb.Table(synth.field_dims(w), emb.EMB_F16, True, 1, w.load_factor, w.acc_init, keys)
+    with pytest.raises(emb.EmbError) as e:
+        T.fill_state(keys.size - 1, 2, rows[:128])
+    assert e.value.name == "EMB_EINVAL"
+    with pytest.raises(emb.EmbError) as e:
+        T.fill_state(-1, 1, rows[:64])
+    assert e.value.name == "EMB_EINVAL"
+    T.fill_state(0, 0)                    # empty range: nothing to do
+    w2 = W.scaled(W.F26, n_keys=20_000, batch=4)
+    T2, keys2, rows2, _ = _table(w2)
+    with pytest.raises(emb.EmbError) as e:
+        T2.fill_state(0, 1, None, None, np.zeros(16, dtype=np.float32))
+    assert e.value.name == "EMB_EINVAL"
