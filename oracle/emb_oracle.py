@@ -147,6 +147,56 @@ def layout_closed_form(keys: np.ndarray, n_home: int) -> Tuple[np.ndarray, np.nd
     return home, slot
 
 
+def slots_of_sample(keys: np.ndarray, n_home: int, sample: np.ndarray,
+                    chunk: int = 1 << 24) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The layout of ``layout_closed_form`` for a few keys of a very large one-table key set,
+    without sorting the set.
+
+    In (home, key) order the i-th key sits at slot_i = max_{j <= i}(home_j + i - j).  Grouping
+    the j by their home x, the best j of a group is its first, whose rank is P(x) = #{keys with
+    home < x}; an x that no key has never beats the max (the first key at or after it does at
+    least as well).  So a key of home h that is preceded by r keys of the same home has
+    rank i = P(h) + r and slot = P(h) + r + max_{0 <= x <= h}(x - P(x)).
+    Only counts of keys per home are needed.  Returns (home, slot, rank) of keys[sample]."""
+    k = np.asarray(keys).view(np.uint64)
+    sample = np.asarray(sample, dtype=np.int64)
+    home = np.empty(k.size, dtype=np.int64)
+    for a in range(0, k.size, chunk):
+        home[a:a + chunk] = home_of(hash64_array(k[a:a + chunk]), n_home)
+    counts = np.bincount(home, minlength=n_home)
+    hs = home[sample]
+    ks = k[sample]
+    # r: keys of the same home with a smaller key
+    cand = np.nonzero(np.isin(home, np.unique(hs)))[0]
+    ch, ck = home[cand], k[cand]
+    order = np.lexsort((ck, ch))
+    ch, ck = ch[order], ck[order]
+    first = np.searchsorted(ch, hs, side="left")
+    r = np.array([int(np.searchsorted(ck[f:f + counts[h]], kk, side="left"))
+                  for f, h, kk in zip(first, hs, ks)], dtype=np.int64)
+    # P(h) and max_{x <= h}(x - P(x)), walking the home range in chunks
+    P_at = np.empty(hs.size, dtype=np.int64)
+    Q_at = np.empty(hs.size, dtype=np.int64)
+    by_home = np.argsort(hs, kind="stable")
+    p_run, q_run, s = 0, -(1 << 62), 0
+    for a in range(0, n_home, chunk):
+        b = min(n_home, a + chunk)
+        c = counts[a:b]
+        P = p_run + np.concatenate([[0], np.cumsum(c)[:-1]])
+        Q = np.maximum(np.maximum.accumulate(np.arange(a, b, dtype=np.int64) - P), q_run)
+        e = s
+        while e < by_home.size and hs[by_home[e]] < b:
+            e += 1
+        sel = by_home[s:e]
+        P_at[sel] = P[hs[sel] - a]
+        Q_at[sel] = Q[hs[sel] - a]
+        s = e
+        p_run = int(P[-1] + c[-1])
+        q_run = int(Q[-1])
+    rank = P_at + r
+    return hs, rank + Q_at, rank
+
+
 def key_array(keys: np.ndarray, slot: np.ndarray, n_home: int) -> np.ndarray:
     """The probed array: EMPTY everywhere except each key at its slot, with at
     least one EMPTY past the last key so every scan ends."""

@@ -172,3 +172,34 @@ def test_multiple_hash_partition():
     assert set(np.unique(t).tolist()) <= {0, 1}
     assert np.all(t == (keys & np.uint64(1)).astype(np.int64))
     assert np.all(O.table_of(keys, 1) == 0)
+
+
+@pytest.mark.parametrize("n,lf,chunk", [(1, 0.5, 1 << 24), (2000, 0.6, 97), (60_000, 0.5, 1000),
+                                        (60_000, 0.95, 4096), (200_000, 1.0, 1 << 24)])
+def test_sampled_slots_equal_full_layout(n, lf, chunk):
+    """The counting form used for very large tables agrees with the sorted closed form (itself
+    pinned by sequential insertion), including clusters that run across the chunks it walks."""
+    r = np.random.default_rng(n + chunk)
+    keys = np.unique(r.integers(0, 1 << 48, size=n, dtype=np.int64)).view(np.uint64)
+    r.shuffle(keys)
+    nh = O.n_home_slots(keys.size, lf)
+    home, slot = O.layout_closed_form(keys, nh)
+    sample = np.unique(r.integers(0, keys.size, size=min(keys.size, 3000)))
+    hs, ss, rank = O.slots_of_sample(keys, nh, sample, chunk=chunk)
+    assert np.array_equal(hs, home[sample])
+    assert np.array_equal(ss, slot[sample])
+    # rank = position in (home, key) order
+    order = np.lexsort((keys, home))
+    pos = np.empty(keys.size, dtype=np.int64)
+    pos[order] = np.arange(keys.size)
+    assert np.array_equal(rank, pos[sample])
+
+
+def test_sampled_slots_on_a_crowded_table_by_insertion():
+    # many keys per home slot: the same-home rank r carries most of the slot
+    keys = np.arange(1, 301, dtype=np.uint64) * np.uint64(0x9E37)
+    nh = 17
+    want = O.layout_by_insertion(keys.tolist(), nh)
+    sample = np.arange(0, 300, 7)
+    _, ss, _ = O.slots_of_sample(keys, nh, sample, chunk=5)
+    assert ss.tolist() == [want[int(k)] for k in keys[sample]]
