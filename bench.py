@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+from concurrent.futures import ThreadPoolExecutor
 import json
 import os
 import subprocess
@@ -60,9 +61,13 @@ def batch_stats(w, bt, dims, rowref):
     bag = np.repeat(np.arange(off.size - 1, dtype=np.int64), np.diff(off.astype(np.int64)))
     width = dims[bag % F].astype(np.int64)           # row width of each occurrence
     rr = rowref.astype(np.int64)
-    order = np.argsort(rr, kind="stable")
-    srr = rr[order]
-    sw = width[order]
+    if np.all(dims == dims[0]):                      # one width: no permutation needed
+        srr = np.sort(rr)
+        sw = width
+    else:
+        order = np.argsort(rr, kind="stable")
+        srr = rr[order]
+        sw = width[order]
     heads = np.concatenate([[True], srr[1:] != srr[:-1]])
     starts = np.nonzero(heads)[0]
     ends = np.concatenate([starts[1:], [srr.size]]) - 1
@@ -134,6 +139,82 @@ def load_traffic(workload, kernel):
         return float(e["bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+# --------------------------------------------------------------------------- table + ring
+def build_table(w, pinned=True):
+    """The workload's prebuilt table with its initial state in the host image.  Tables of 64M+
+    keys are created without state and filled field by field on a thread pool, so the state is
+    never held twice on the host.  Returns (Table, keys, pinned)."""
+    from ad_recommendation_amd import emb
+    from gen import synth
+    dims = synth.field_dims(w)
+    rdt = emb.EMB_F16 if w.row_dtype == "f16" else emb.EMB_F32
+    t0 = time.perf_counter()
+    keys = synth.resident_keys(w)
+    big = w.n_keys >= (1 << 26)
+    if big:
+        log(f"[bench] {keys.size} resident keys drawn in {time.perf_counter() - t0:.0f}s")
+
+    def make(flags):
+        if not big:
+            rows, master = synth.initial_state(w)
+            return emb.Table(dims, rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init,
+                             keys, rows, None, master, flags=flags)
+        return emb.Table(dims, rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init, keys,
+                         flags=flags)
+    T = None
+    if pinned:
+        try:  # pinned host image: the PASS flash is one DMA from page-locked memory
+            T = make(emb.FLAG_PINNED_STAGING)
+        except emb.EmbError as e:
+            log(f"[bench] pinned host image unavailable ({e}); using pageable memory")
+    if T is None:
+        T, pinned = make(0), False
+    if big:
+        log(f"[bench] table created in {time.perf_counter() - t0:.0f}s; filling state by field")
+        foff = synth.field_key_offsets(w)
+
+        def fill(f):
+            r_f, m_f = synth.field_state(w, f)
+            T.fill_state(int(foff[f]), int(foff[f + 1] - foff[f]), r_f, None, m_f)
+        with ThreadPoolExecutor(max(1, min(8, synth.worker_count()))) as ex:
+            list(ex.map(fill, range(w.n_fields)))
+    return T, keys, pinned
+
+
+def host_batch(w, T, dims, b):
+    """Batch b with the byte-model statistics of its occurrences (host side)."""
+    from ad_recommendation_amd import emb
+    from gen import synth
+    bt = synth.batch(w, b)
+    rr, _ = emb.table_key_rowref(T.h, bt["keys"])
+    bt["st"] = batch_stats(w, bt, dims, rr)
+    return bt
+
+
+def stage_ring(w, T, dims, R, dev):
+    """R batches generated on the host (in parallel waves for large batches) and copied to HBM."""
+    import torch
+    from gen import synth
+    ring = []
+    workers = min(8, synth.worker_count()) if w.batch * w.n_fields >= (1 << 22) else 1
+    for a in range(0, R, max(1, workers)):
+        idx = list(range(a, min(R, a + max(1, workers))))
+        if workers > 1:
+            with ThreadPoolExecutor(workers) as ex:
+                got = list(ex.map(lambda b: host_batch(w, T, dims, b), idx))
+        else:
+            got = [host_batch(w, T, dims, b) for b in idx]
+        for bt in got:
+            ring.append({
+                "keys": torch.from_numpy(bt["keys"]).to(dev),
+                "offsets": torch.from_numpy(bt["offsets"]).to(dev),
+                "grad": torch.from_numpy(bt["grad"]).to(dev),
+                "n_bags": bt["offsets"].size - 1, "nnz": bt["st"]["nnz"], "st": bt["st"],
+            })
+        del got
+    return ring
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -220,26 +301,12 @@ def main():
         print(json.dumps({"copy_calibration_bytes": args.copy_calibration}), flush=True)
         return
     w = W.get(args.workload)
-    R = args.ring or min(w.ring, 16)
+    R = args.ring or w.ring
     dims = synth.field_dims(w)
     t0 = time.perf_counter()
-    keys = synth.resident_keys(w)
-    rows, master = synth.initial_state(w)
-    log(f"[bench] {w.name}: {keys.size} keys generated in {time.perf_counter() - t0:.1f}s")
-    t0 = time.perf_counter()
-    rdt = emb.EMB_F16 if w.row_dtype == "f16" else emb.EMB_F32
-    try:  # pinned host image: the PASS flash is one DMA from page-locked memory
-        T = emb.Table(dims, rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init, keys, rows,
-                      None, master, flags=emb.FLAG_PINNED_STAGING)
-        pinned = True
-    except emb.EmbError as e:
-        log(f"[bench] pinned host image unavailable ({e}); using pageable memory")
-        T = emb.Table(dims, rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init, keys, rows,
-                      None, master)
-        pinned = False
-    del rows, master
-    log(f"[bench] table built in {time.perf_counter() - t0:.1f}s; arena "
-        f"{T.info['arena_bytes'] / 2**30:.2f} GiB")
+    T, keys, pinned = build_table(w)
+    log(f"[bench] {w.name}: {keys.size} keys, table built in {time.perf_counter() - t0:.1f}s; "
+        f"arena {T.info['arena_bytes'] / 2**30:.2f} GiB")
     T.arena = torch.empty(emb.table_device_bytes(T.h), dtype=torch.uint8, device=dev)
     flash_ms = []
     for _ in range(2):  # the PASS flash (host image -> HBM), timed on its own
@@ -256,33 +323,24 @@ def main():
     odt = torch.float16 if w.out_dtype == "f16" else torch.float32
     out_code = emb.EMB_F16 if w.out_dtype == "f16" else emb.EMB_F32
     g_code = emb.EMB_F16 if w.grad_dtype == "f16" else emb.EMB_F32
-    ring = []
-    ws_bytes = 0
-    for b in range(R):
-        bt = synth.batch(w, b)
-        rr, _ = emb.table_key_rowref(T.h, bt["keys"])
-        st = batch_stats(w, bt, dims, rr)
-        n_bags = bt["offsets"].size - 1
-        ring.append({
-            "keys": torch.from_numpy(bt["keys"]).to(dev),
-            "offsets": torch.from_numpy(bt["offsets"]).to(dev),
-            "grad": torch.from_numpy(bt["grad"]).to(dev),
-            "out": torch.empty(w.batch, int(dims.sum()), dtype=odt, device=dev),
-            "rowref": torch.empty(max(1, st["nnz"]), dtype=torch.int32, device=dev),
-            "n_bags": n_bags, "nnz": st["nnz"], "st": st,
-        })
-        ws_bytes = max(ws_bytes, emb.bwd_workspace_bytes(T.h, n_bags, st["nnz"]))
+    t0 = time.perf_counter()
+    ring = stage_ring(w, T, dims, R, dev)
+    max_nnz = max(r["nnz"] for r in ring)
+    ws_bytes = max(emb.bwd_workspace_bytes(T.h, r["n_bags"], r["nnz"]) for r in ring)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(w.batch, int(dims.sum()), dtype=odt, device=dev)   # shared by the ring
+    rowref = torch.empty(max(1, max_nnz), dtype=torch.int32, device=dev)
     n_unique = torch.zeros(R, dtype=torch.int64, device=dev)
     rowref_space = T.info["rowref_space"]
-    log(f"[bench] ring of {R} batches staged; mean nnz {np.mean([r['nnz'] for r in ring]):.0f}, "
-        f"mean unique {np.mean([r['st']['U'] for r in ring]):.0f}")
+    log(f"[bench] ring of {R} batches staged in {time.perf_counter() - t0:.1f}s; mean nnz "
+        f"{np.mean([r['nnz'] for r in ring]):.0f}, mean unique "
+        f"{np.mean([r['st']['U'] for r in ring]):.0f}")
 
     def step(i):
         r = ring[i % R]
-        emb.lookup_pool_fwd(T.h, r["keys"], r["offsets"], r["n_bags"], r["nnz"], r["out"],
-                            out_code, r["rowref"])
-        emb.sparse_adagrad_bwd(T.h, r["rowref"], r["offsets"], r["n_bags"], r["nnz"], r["grad"],
+        emb.lookup_pool_fwd(T.h, r["keys"], r["offsets"], r["n_bags"], r["nnz"], out,
+                            out_code, rowref)
+        emb.sparse_adagrad_bwd(T.h, rowref, r["offsets"], r["n_bags"], r["nnz"], r["grad"],
                                g_code, w.lr, w.eps, ws, n_unique=n_unique[i % R:i % R + 1])
 
     for i in range(args.warmup):

@@ -166,27 +166,29 @@ def slots_of_sample(keys: np.ndarray, n_home: int, sample: np.ndarray,
     counts = np.bincount(home, minlength=n_home)
     hs = home[sample]
     ks = k[sample]
-    # r: keys of the same home with a smaller key
-    cand = np.nonzero(np.isin(home, np.unique(hs)))[0]
-    ch, ck = home[cand], k[cand]
-    order = np.lexsort((ck, ch))
-    ch, ck = ch[order], ck[order]
-    first = np.searchsorted(ch, hs, side="left")
-    r = np.array([int(np.searchsorted(ck[f:f + counts[h]], kk, side="left"))
-                  for f, h, kk in zip(first, hs, ks)], dtype=np.int64)
+    # r: keys of the same home with a smaller key (candidates found chunk by chunk)
+    wanted = np.zeros(n_home, dtype=bool)
+    wanted[hs] = True
+    cand = np.concatenate([a + np.nonzero(wanted[home[a:a + chunk]])[0]
+                           for a in range(0, k.size, chunk)])
+    del wanted              # ascending positions, the sample among them
+    order = np.lexsort((k[cand], home[cand]))      # candidates in (home, key) order
+    place = np.empty(cand.size, dtype=np.int64)
+    place[order] = np.arange(cand.size)
+    first = np.searchsorted(home[cand][order], hs, side="left")
+    r = place[np.searchsorted(cand, sample)] - first
     # P(h) and max_{x <= h}(x - P(x)), walking the home range in chunks
     P_at = np.empty(hs.size, dtype=np.int64)
     Q_at = np.empty(hs.size, dtype=np.int64)
     by_home = np.argsort(hs, kind="stable")
+    hs_sorted = hs[by_home]
     p_run, q_run, s = 0, -(1 << 62), 0
     for a in range(0, n_home, chunk):
         b = min(n_home, a + chunk)
         c = counts[a:b]
         P = p_run + np.concatenate([[0], np.cumsum(c)[:-1]])
         Q = np.maximum(np.maximum.accumulate(np.arange(a, b, dtype=np.int64) - P), q_run)
-        e = s
-        while e < by_home.size and hs[by_home[e]] < b:
-            e += 1
+        e = int(np.searchsorted(hs_sorted, b, side="left"))
         sel = by_home[s:e]
         P_at[sel] = P[hs[sel] - a]
         Q_at[sel] = Q[hs[sel] - a]

@@ -1,0 +1,156 @@
+"""Parity at the full PASS scale: 800M resident keys in one unified table (dim 32, fp16 rows,
+fp32 accumulators, ~167 GB in HBM), one batch of 131,072 samples x 64 fields (~50M lookups),
+in the launch configuration the benchmark times.
+
+The oracle cannot hold this table, so it checks samples it computes one by one:
+  * slots and rowrefs of 20,000 sampled occurrences, bit-exact, from per-home key counts
+    (``oracle.slots_of_sample``) rather than a sort of all 800M keys;
+  * the pooled output of 1 bag in 64, within the fp16 tolerance;
+  * the number of distinct rows touched, bit-exact, and the count of sampled unique rows;
+  * rows and accumulators of 1 % of the touched keys after the update, within the derived
+    budgets, and sampled untouched keys bit-identical.
+For the pooled and update checks the oracle is a table over just the keys those samples need
+(every key of the sampled bags and every sampled touched key); keys outside it only act as
+misses there, which changes neither the sampled bags nor the sampled rows' gradients.
+
+Opt-in (EMB_PASS_SCALE=1): building the table takes minutes and ~200 GB of host memory.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from ad_recommendation_amd import emb  # noqa: E402
+from gen import synth, workloads as W  # noqa: E402
+from oracle import emb_oracle as O  # noqa: E402
+from tests import parity_util as P  # noqa: E402
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(os.environ.get("EMB_PASS_SCALE") != "1",
+                                 reason="800M-key table: set EMB_PASS_SCALE=1 (minutes, ~200 GB host)")]
+
+
+def say(*a):
+    print("[pass-scale]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def positions(keys, want, chunk=1 << 24):
+    """Index in `keys` of each of the sorted distinct keys `want` (each must occur once), in one
+    pass over `keys` without sorting it."""
+    pos = np.full(want.size, -1, dtype=np.int64)
+    low = np.uint64((1 << 28) - 1)
+    maybe = np.zeros(1 << 28, dtype=bool)            # filter on the low 28 bits first
+    maybe[(want & low).astype(np.intp)] = True
+    for a in range(0, keys.size, chunk):
+        kc = keys[a:a + chunk]
+        c = np.nonzero(maybe[(kc & low).astype(np.intp)])[0]
+        i = np.minimum(np.searchsorted(want, kc[c]), want.size - 1)
+        hit = want[i] == kc[c]
+        pos[i[hit]] = a + c[hit]
+    assert np.all(pos >= 0)
+    return pos
+
+
+def initial_rows(w, pos, D):
+    """Initial rows of the resident keys at positions `pos` (fields regenerated one by one)."""
+    foff = synth.field_key_offsets(w)
+    out = np.empty((pos.size, D), dtype=np.float16)
+    for f in range(w.n_fields):
+        sel = np.nonzero((pos >= foff[f]) & (pos < foff[f + 1]))[0]
+        if sel.size == 0:
+            continue
+        r_f, _ = synth.field_state(w, f)
+        out[sel] = r_f.reshape(-1, D)[pos[sel] - foff[f]]
+    return out.reshape(-1)
+
+
+def test_pass_scale_sampled_parity():
+    import bench
+    from tests.test_gpu_parity import gpu_step
+    w = W.F64_PASS
+    dims = synth.field_dims(w)
+    D = int(dims[0])
+    F = w.n_fields
+    t0 = time.perf_counter()
+    T, keys, pinned = bench.build_table(w)
+    say(f"table of {keys.size} keys built and filled in {time.perf_counter() - t0:.0f}s "
+        f"(pinned={pinned}); arena {T.info['arena_bytes'] / 1e9:.1f} GB")
+    t0 = time.perf_counter()
+    T.flash()
+    torch.cuda.synchronize()
+    say(f"flashed in {time.perf_counter() - t0:.1f}s")
+    bt = synth.batch(w, 0)
+    bkeys = bt["keys"].view(np.uint64)
+    nnz = bkeys.size
+    say(f"batch 0: {nnz} lookups")
+    res = gpu_step(T, bt["keys"], bt["offsets"], bt["grad"], w.out_dtype, w.grad_dtype, w.lr,
+                   w.eps)
+    say(f"GPU step done: {res['n_unique']} unique rows, {res['n_miss']} misses")
+    emb.pass_writeback(T.h)
+    say("state written back")
+    assert res["n_miss"] == 0
+
+    r = np.random.default_rng(7)
+    bk, bcount = np.unique(bkeys, return_counts=True)
+    assert res["n_unique"] == bk.size
+    uq = res["unique"].astype(np.int64)
+    assert np.all(np.diff(uq) > 0)
+    # samples: occurrences (slots), 1 % of touched keys (counts, update), 1 bag in 64 (pooling)
+    occ = np.unique(r.integers(0, nnz, size=20_000))
+    pick = np.unique(r.integers(0, bk.size, size=max(1, bk.size // 100)))
+    pick_keys = bk[pick]
+    bags = np.arange(0, bt["offsets"].size - 1, 64)
+    off64 = bt["offsets"].astype(np.int64)
+    bag_occ = np.concatenate([np.arange(off64[j], off64[j + 1]) for j in bags])
+    need = np.unique(np.concatenate([bkeys[bag_occ], pick_keys]))
+    want = np.unique(np.concatenate([bkeys[occ], need]))
+    t0 = time.perf_counter()
+    wpos = positions(keys, want)
+    say(f"{want.size} sampled keys located in {time.perf_counter() - t0:.0f}s")
+
+    # ---- slots and rowrefs, bit-exact (one row per granule: rowref = rank in slot order)
+    nh = O.n_home_slots(keys.size, w.load_factor)
+    t0 = time.perf_counter()
+    _, slot_o, rank_o = O.slots_of_sample(keys, nh, wpos)
+    say(f"oracle slots of {want.size} keys in {time.perf_counter() - t0:.0f}s")
+    at = np.searchsorted(want, bkeys[occ])
+    assert np.array_equal(res["slot"][occ], slot_o[at])
+    assert np.array_equal(res["rowref"][occ].astype(np.int64), rank_o[at])
+    # the unique list holds each sampled touched key's rowref, with its occurrence count
+    pr = rank_o[np.searchsorted(want, pick_keys)]
+    u_at = np.searchsorted(uq, pr)
+    assert np.array_equal(uq[u_at], pr)
+    assert np.array_equal(res["count"][u_at], bcount[pick])
+    say(f"{occ.size} slots, {pick.size} unique rows and counts match")
+
+    # ---- oracle over the keys the samples need
+    npos = wpos[np.searchsorted(want, need)]
+    ot = O.Table(need, dims, w.row_dtype, w.has_master, 1, w.load_factor, w.acc_init,
+                 initial_rows(w, npos, D))
+    say(f"oracle table over {need.size} keys")
+    pooled, _ = ot.forward(bt["keys"], bt["offsets"], w.out_dtype, bags=bags)
+    S = P.pooled_scale(ot, bt["keys"], bt["offsets"])
+    for j, v in pooled.items():
+        b, f = divmod(j, F)
+        P.check_pooled(res["out"][b, f * D:(f + 1) * D][None, :], v[None, :],
+                       S[b, f * D:(f + 1) * D][None, :], w.out_dtype)
+    say(f"{len(pooled)} sampled bags pooled within tolerance")
+    del S
+
+    bud = P.Budget(ot)
+    bud.oracle_step(ot, bt["keys"], bt["offsets"], bt["grad"], w.lr, w.eps)
+    rows_g, acc_g, _ = T.export(pick_keys)
+    P.check_state(ot, bud, pick_keys, rows_g, acc_g, None)
+    # untouched resident keys: bit-identical to their initial state
+    upos = np.unique(r.integers(0, keys.size, size=5000))
+    upos = upos[~np.isin(keys[upos], bk)]
+    ru, au, _ = T.export(keys[upos])
+    assert np.all(au == np.float32(w.acc_init))
+    assert ru.tobytes() == initial_rows(w, upos, D).tobytes()
+    say(f"{pick.size} updated rows within budget; {upos.size} untouched rows bit-identical")
+    T.close()
