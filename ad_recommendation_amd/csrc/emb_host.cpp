@@ -33,7 +33,11 @@ int fail(int code, const std::string& msg) {
   return code;
 }
 
+// A failed HIP call also leaves its code as the thread's "last error", which the next caller to
+// ask (torch, after its own successful calls) would take as its own failure; clear it here, since
+// the code travels back through the return value and emb_last_error().
 int hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();
   return fail(EMB_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 

@@ -697,9 +697,10 @@ constexpr int kPieceMax = 256;  // occurrences per update piece, at most
 // ends inside the piece is applied at its last occurrence.  The piece's first segment, when it
 // began in an earlier piece, is left as a head partial; its last segment, when it runs into the
 // next piece, as a tail partial; k_update_fixup joins them.  Each batch of rounds issues its
-// gradient-slice loads together with the state of the rows that end in the batch.
+// gradient-slice loads together with the state of the rows that end in the batch.  The kernel is
+// held to 128 VGPRs (four waves per SIMD instead of three) at the cost of a few spilled values.
 template <typename RowT, typename GradT, bool VAR, bool MASTER>
-__global__ __launch_bounds__(kBlock) void k_update_pieces(UpdArgs a, int gs_log2) {
+__global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   constexpr int BR = SegBatch<EPL>::value;
   constexpr int kStage = (kPieceMax + 2 + 63) / 64;

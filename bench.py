@@ -214,6 +214,8 @@ def stage_ring(w, T, dims, R, dev):
                 "n_bags": bt["offsets"].size - 1, "nnz": bt["st"]["nnz"], "st": bt["st"],
             })
         del got
+        if workers > 1:
+            log(f"[bench] {len(ring)}/{R} batches staged")
     return ring
 
 
@@ -277,6 +279,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="f26")
     ap.add_argument("--ring", type=int, default=0, help="distinct batches cycled (0 = workload's)")
+    ap.add_argument("--keys", type=int, default=0,
+                    help="resident keys (0 = the workload's; other values give a scaled copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES, five times (counter scaling)")
@@ -301,6 +305,8 @@ def main():
         print(json.dumps({"copy_calibration_bytes": args.copy_calibration}), flush=True)
         return
     w = W.get(args.workload)
+    if args.keys and args.keys != w.n_keys:
+        w = W.scaled(w, n_keys=args.keys, name_suffix=f"_keys{args.keys}")
     R = args.ring or w.ring
     dims = synth.field_dims(w)
     t0 = time.perf_counter()
