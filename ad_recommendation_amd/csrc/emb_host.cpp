@@ -199,6 +199,12 @@ struct EmbTable {
   size_t off_keys = 0, off_rows = 0, off_acc = 0, off_master = 0, off_meta = 0, arena_bytes = 0;
   uint8_t* image = nullptr;
   bool pinned = false;
+  // pageable images move through two pinned bounce buffers (host copy of one chunk overlaps the
+  // DMA of the other); allocated at the first such copy, null when pinning failed
+  static constexpr size_t kBounce = 256u << 20;
+  uint8_t* bounce[2] = {nullptr, nullptr};
+  hipEvent_t bounce_ev[2] = {nullptr, nullptr};
+  bool bounce_tried = false;
   std::vector<uint64_t> row_keys;  // keys in rowref order
   std::vector<uint32_t> row_ref;   // their rowrefs (ascending)
   std::vector<uint32_t> row_of_key;  // position in row_keys of the i-th key given at create
@@ -272,7 +278,33 @@ struct EmbTable {
     return false;
   }
 
+  bool ensure_bounce() {
+    if (bounce_tried) return bounce[1] != nullptr;
+    bounce_tried = true;
+    for (int i = 0; i < 2; ++i) {
+      if (hipHostMalloc(reinterpret_cast<void**>(&bounce[i]), kBounce, 0) != hipSuccess ||
+          hipEventCreateWithFlags(&bounce_ev[i], hipEventDisableTiming) != hipSuccess) {
+        (void)hipGetLastError();
+        release_bounce();
+        return false;
+      }
+    }
+    return true;
+  }
+  void release_bounce() {
+    for (int i = 0; i < 2; ++i) {
+      if (bounce_ev[i]) {
+        (void)hipEventSynchronize(bounce_ev[i]);
+        (void)hipEventDestroy(bounce_ev[i]);
+        bounce_ev[i] = nullptr;
+      }
+      if (bounce[i]) (void)hipHostFree(bounce[i]);
+      bounce[i] = nullptr;
+    }
+  }
+
   ~EmbTable() {
+    release_bounce();
     for (auto& r : timing.pool) {
       (void)hipEventDestroy(r.a);
       (void)hipEventDestroy(r.b);
@@ -283,6 +315,63 @@ struct EmbTable {
     }
   }
 };
+
+// Host copy spread over threads (a pageable image chunk into or out of a bounce buffer).
+void par_copy(uint8_t* dst, const uint8_t* src, size_t n) {
+  const int T = std::max(1, std::min(n_threads(), (int)(n >> 22)));  // at least 4 MiB a thread
+  const size_t part = ((n + T - 1) / T + 4095) & ~(size_t)4095;
+  std::vector<std::thread> th;
+  for (int i = 0; i < T; ++i) {
+    const size_t o = (size_t)i * part;
+    if (o >= n) break;
+    th.emplace_back([=] { std::memcpy(dst + o, src + o, std::min(part, n - o)); });
+  }
+  for (auto& x : th) x.join();
+}
+
+// Host image -> device through the bounce buffers: chunk k is copied into buffer k % 2 once the
+// DMA that last read that buffer has finished, then its DMA is enqueued on the stream.
+hipError_t flash_bounced(EmbTable* t, uint8_t* d, const uint8_t* h, size_t n, hipStream_t st) {
+  const size_t C = EmbTable::kBounce;
+  for (size_t o = 0, k = 0; o < n; o += C, ++k) {
+    const int b = (int)(k & 1);
+    const size_t len = std::min(C, n - o);
+    hipError_t e = hipEventSynchronize(t->bounce_ev[b]);
+    if (e != hipSuccess) return e;
+    par_copy(t->bounce[b], h + o, len);
+    e = hipMemcpyAsync(d + o, t->bounce[b], len, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(t->bounce_ev[b], st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Device -> host image through the bounce buffers: the DMA of chunk k + 1 runs while chunk k is
+// copied out of its buffer.
+hipError_t writeback_bounced(EmbTable* t, uint8_t* h, const uint8_t* d, size_t n, hipStream_t st) {
+  const size_t C = EmbTable::kBounce;
+  const size_t chunks = (n + C - 1) / C;
+  hipError_t e = hipSuccess;
+  auto issue = [&](size_t k) {
+    const int b = (int)(k & 1);
+    const size_t o = k * C, len = std::min(C, n - o);
+    hipError_t r = hipMemcpyAsync(t->bounce[b], d + o, len, hipMemcpyDeviceToHost, st);
+    if (r == hipSuccess) r = hipEventRecord(t->bounce_ev[b], st);
+    return r;
+  };
+  if (chunks) e = issue(0);
+  for (size_t k = 0; k < chunks && e == hipSuccess; ++k) {
+    if (k + 1 < chunks) e = issue(k + 1);
+    if (e != hipSuccess) break;
+    const int b = (int)(k & 1);
+    e = hipEventSynchronize(t->bounce_ev[b]);
+    if (e != hipSuccess) break;
+    const size_t o = k * C;
+    par_copy(h + o, t->bounce[b], std::min(C, n - o));
+  }
+  return e;
+}
 
 extern "C" {
 
@@ -551,8 +640,12 @@ int pass_flash(EmbTable* t, void* d_arena, size_t arena_bytes, emb_stream_t stre
   if (!t || !d_arena) return fail(EMB_EINVAL, "null table or arena");
   if (reinterpret_cast<uintptr_t>(d_arena) % 256) return fail(EMB_EINVAL, "arena must be 256-byte aligned");
   if (arena_bytes < t->arena_bytes) return fail(EMB_ENOSPACE, "arena smaller than table_device_bytes()");
-  hipError_t e = hipMemcpyAsync(d_arena, t->image, t->arena_bytes, hipMemcpyHostToDevice,
-                                static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!t->pinned && t->arena_bytes > EmbTable::kBounce && t->ensure_bounce())
+    e = flash_bounced(t, static_cast<uint8_t*>(d_arena), t->image, t->arena_bytes, st);
+  else
+    e = hipMemcpyAsync(d_arena, t->image, t->arena_bytes, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_fail(e, "pass_flash copy");
   t->d_arena = static_cast<uint8_t*>(d_arena);
   t->flashed = true;
@@ -642,8 +735,12 @@ int pass_writeback(EmbTable* t, emb_stream_t stream) {
   if (!t->flashed) return fail(EMB_ESTATE, "write-back before pass_flash");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t n = t->off_meta - t->off_rows;
-  hipError_t e = hipMemcpyAsync(t->image + t->off_rows, t->d_arena + t->off_rows, n,
-                                hipMemcpyDeviceToHost, s);
+  hipError_t e;
+  if (!t->pinned && n > EmbTable::kBounce && t->ensure_bounce())
+    e = writeback_bounced(t, t->image + t->off_rows, t->d_arena + t->off_rows, n, s);
+  else
+    e = hipMemcpyAsync(t->image + t->off_rows, t->d_arena + t->off_rows, n,
+                       hipMemcpyDeviceToHost, s);
   if (e != hipSuccess) return hip_fail(e, "pass_writeback copy");
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "pass_writeback sync");

@@ -113,7 +113,11 @@ int table_device_bytes(const EmbTable* t, size_t* bytes);
  * caller's device arena in one bulk host-to-device copy, enqueued on `stream`.  The arena must be
  * 256-byte aligned and at least table_device_bytes() long (EMB_ENOSPACE).  The arena stays bound
  * to the table until the next pass_flash or table_destroy; rowrefs from an earlier flash are
- * invalid afterwards.  With a pageable host image the copy is synchronous with respect to the host.
+ * invalid afterwards.  A pinned host image (EMB_FLAG_PINNED_STAGING) goes over in one DMA and the
+ * call returns once it is enqueued.  A pageable image goes through two 256 MiB pinned bounce
+ * buffers owned by the table (allocated at the first such copy; a plain copy when that fails):
+ * the host copies one chunk while the DMA of the previous one runs, so the call returns only once
+ * the last chunk is enqueued.
  */
 int pass_flash(EmbTable* t, void* d_arena, size_t arena_bytes, emb_stream_t stream);
 
@@ -166,7 +170,8 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
 
 /*
  * Copy rows, accumulators and masters from the device arena back into the table's host image
- * (the end-of-PASS write-back).  Synchronises `stream`.
+ * (the end-of-PASS write-back).  Synchronises `stream`.  A pageable image is filled through the
+ * same bounce buffers as pass_flash (the DMA of one chunk overlaps the host copy of the other).
  */
 int pass_writeback(EmbTable* t, emb_stream_t stream);
 
