@@ -677,6 +677,7 @@ int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets
   a.rowref = d_rowref;
   a.slot = d_slot;
   a.n_miss = reinterpret_cast<unsigned long long*>(d_n_miss);
+  a.probe = (t->flags & EMB_FLAG_PROBE_COOP) ? 1 : (t->flags & EMB_FLAG_PROBE_LANE) ? 2 : 0;
   LaunchCtx ctx{static_cast<hipStream_t>(stream), &t->timing};
   hipError_t e = launch_lookup_pool(a, ctx);
   if (e != hipSuccess) return hip_fail(e, "lookup_pool_fwd launch");

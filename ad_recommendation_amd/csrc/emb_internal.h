@@ -95,6 +95,7 @@ struct FwdLaunch {
   uint32_t* rowref;
   int64_t* slot;
   unsigned long long* n_miss;
+  int32_t probe;  // 0: by bucket-array size, 1: wave-cooperative, 2: per-lane
 };
 
 struct BwdLaunch {

@@ -121,6 +121,10 @@ __device__ __forceinline__ uint32_t div_fields(const DevDesc& d, uint32_t n) {
 // Ordered linear probing over 128-byte buckets of 15 keys: scan from the home slot until the key
 // or an empty slot.  On a hit the rowref is the bucket's stored prefix plus the row units of the
 // occupied slots before the hit (rows are stored in slot order).
+//
+// Two forms.  In the per-lane form below, one lane reads its key's whole bucket (eight 16-byte
+// loads); it needs the least work per key and is the faster one while the table's buckets stay
+// within the reach of the address-translation caches.
 template <bool VAR>
 __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, int bag_field,
                                               int64_t& slot) {
@@ -169,9 +173,67 @@ __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, in
   }
 }
 
+// In the wave-cooperative form, the eight lanes of a lane group read one bucket together, lane s
+// loading 16 bytes (slots 2s and 2s+1; lane 7's second word is the prefix), so one load
+// instruction touches eight buckets instead of 64.  It costs more instructions per key, but when
+// the buckets span more memory than the translation caches reach, each of the per-lane form's
+// eight instructions re-misses on 64 pages.  Measured on MI355X: random 128-byte lines read by
+// one lane each come at ~10 G lines/s against ~48 G lines/s read by eight lanes each.  On the
+// 64-field, batch-131072 forward the cooperative form takes 2.7-2.9 ms at 200M, 400M and 800M
+// keys (3.4, 6.8 and 13.6 GB of buckets) where the per-lane form takes 3.4, 5.2 and 5.8 ms; the
+// per-lane form takes 2.0 ms at 100M keys (1.7 GB), and on a 50M-key table with 0.7 GB of buckets
+// it is the faster one (1.35 against 2.18 ms on the 100-field forward).  Hence the 2 GiB switch.
+struct BucketHit {
+  bool stop;      // the key or an empty slot was found in this bucket
+  uint32_t rr;    // rowref on a hit, kMiss otherwise
+  int l;          // slot within the bucket on a hit
+};
+
+// Evaluates one bucket for the group's key `key` from the group's loaded words (this lane's
+// slots 2*sub, 2*sub+1), scanning from slot l0.  Every lane of the wave must call it (it uses
+// cross-lane operations); the result is uniform within each lane group.
+template <bool VAR>
+__device__ __forceinline__ BucketHit eval_bucket(const DevDesc& d, u64x2 v, uint64_t key, int l0,
+                                                 int sub, int grp) {
+  const bool last = sub == 7;  // this lane's second word is the prefix, not a slot
+  const uint32_t m = (uint32_t)(v.x == key) | ((uint32_t)(!last && v.y == key) << 1);
+  const uint32_t o = (uint32_t)(v.x != kEmpty) | ((uint32_t)(!last && v.y != kEmpty) << 1);
+  uint32_t packed = (m << (2 * sub)) | (o << (16 + 2 * sub));
+  packed |= __shfl_xor(packed, 1, 64);
+  packed |= __shfl_xor(packed, 2, 64);
+  packed |= __shfl_xor(packed, 4, 64);
+  const uint32_t match = packed & 0x7FFFu, occ = (packed >> 16) & 0x7FFFu;
+  const uint32_t prefix = (uint32_t)__shfl((unsigned long long)v.y, grp * 8 + 7, 64);
+  const uint32_t stop = (match | (~occ & 0x7FFFu)) & ((0x7FFFu << l0) & 0x7FFFu);
+  BucketHit h;
+  h.stop = stop != 0;
+  h.l = stop ? __builtin_ctz(stop) : 0;
+  const bool hit = h.stop && ((match >> h.l) & 1u);
+  const uint32_t below = occ & ((1u << h.l) - 1u);
+  uint32_t units;
+  if (!VAR) {
+    units = __builtin_popcount(below);
+  } else {
+    // row units of the occupied slots before the hit, summed over the group's lanes
+    // (the field index is selected before the table read: an empty slot's field bits are 0xFFFF)
+    const bool u0 = (below >> (2 * sub)) & 1u, u1 = (below >> (2 * sub + 1)) & 1u;
+    const uint32_t g0 = (uint32_t)d.fgran[u0 ? (int)(v.x >> 48) : 0];
+    const uint32_t g1 = (uint32_t)d.fgran[u1 ? (int)(v.y >> 48) : 0];
+    units = (u0 ? g0 : 0u) + (u1 ? g1 : 0u);
+    units += __shfl_xor(units, 1, 64);
+    units += __shfl_xor(units, 2, 64);
+    units += __shfl_xor(units, 4, 64);
+  }
+  h.rr = hit ? prefix + units : kMiss;
+  return h;
+}
+
 // ---------------------------------------------------------------- forward: probe + sum pool
 constexpr int kFwdBags = 64;     // bags per block
 constexpr int kFwdKeyCap = 2048; // rowrefs staged in LDS; larger blocks re-read them from HBM/L2
+constexpr int kProbeRounds = 8;  // buckets in flight per lane group: a wave probes 64 keys at once
+// bucket arrays at least this large are probed in the wave-cooperative form
+constexpr uint64_t kCoopProbeBytes = 2ull << 30;
 
 // Gathers and sums the rows of bag jb's occurrences k0..k1 (rowrefs from `rr`), EPL elements per
 // lane, four rows in flight; misses read row 0 and are dropped.
@@ -197,12 +259,15 @@ __device__ __forceinline__ typename F32V<16 / sizeof(RowT)>::t pool_rows(const D
   return acc;
 }
 
-template <typename RowT, typename OutT, bool VAR>
+template <typename RowT, typename OutT, bool VAR, bool COOP>
 __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   typedef typename F32V<EPL>::t AccV;
   __shared__ int32_t s_off[kFwdBags + 1];
   __shared__ uint32_t s_rr[kFwdKeyCap];
+  __shared__ uint64_t s_pk[kWaves][64];          // keys of the wave's chunk (EMPTY: no probe)
+  __shared__ uint32_t s_pb[kWaves][64];          // their home buckets
+  __shared__ uint32_t s_pl[kWaves][64];          // home lane, table, buckets after the home one
   __shared__ uint32_t s_miss;
   const int tid = threadIdx.x;
   const int32_t j0 = (int32_t)blockIdx.x * kFwdBags;
@@ -217,24 +282,117 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   const int F = a.d.n_fields;
   const int f0 = (int)((uint32_t)j0 - div_fields(a.d, (uint32_t)j0) * (uint32_t)F);
 
-  // phase 1: one lane per key
   uint32_t miss = 0;
-  for (int i = tid; i < nk; i += kBlock) {
-    const int32_t pos = base + i;
-    const uint64_t key = (uint64_t)a.keys[pos];
-    int lo = 0, hi = nb - 1;  // last bag whose start is <= pos
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
+  if (!COOP) {
+    // phase 1, per-lane form: one lane per key
+    for (int i = tid; i < nk; i += kBlock) {
+      const int32_t pos = base + i;
+      const uint64_t key = (uint64_t)a.keys[pos];
+      int lo = 0, hi = nb - 1;  // last bag whose start is <= pos
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
+      }
+      int bf = f0 + lo;
+      bf = bf >= F ? bf - (int)div_fields(a.d, (uint32_t)bf) * F : bf;
+      int64_t sl;
+      const uint32_t rr = probe_key<VAR>(a.d, key, bf, sl);
+      miss += (rr == kMiss);
+      if (in_lds) s_rr[i] = rr;
+      a.rowref[pos] = rr;
+      if (a.slot) a.slot[pos] = sl;
     }
-    int bf = f0 + lo;
-    bf = bf >= F ? bf - (int)div_fields(a.d, (uint32_t)bf) * F : bf;
-    int64_t sl;
-    const uint32_t rr = probe_key<VAR>(a.d, key, bf, sl);
-    miss += (rr == kMiss);
-    if (in_lds) s_rr[i] = rr;
-    a.rowref[pos] = rr;
-    if (a.slot) a.slot[pos] = sl;
+  } else {
+    // phase 1, wave-cooperative form: each wave probes chunks of 64 keys, eight buckets per load
+    // instruction
+    const int w = tid >> 6, lane = lane_id(), grp = lane >> 3, sub = lane & 7;
+    for (int c0 = w * 64; c0 < nk; c0 += kBlock) {
+      // one lane per key: its field check, hash and home bucket, staged for the lane groups
+      {
+        const int i = c0 + lane;
+        uint64_t key = kEmpty;  // no probe: past the block's keys, or a miss by construction
+        if (i < nk) {
+          const int32_t pos = base + i;
+          key = (uint64_t)a.keys[pos];
+          int lo = 0, hi = nb - 1;  // last bag whose start is <= pos
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
+          }
+          int bf = f0 + lo;
+          bf = bf >= F ? bf - (int)div_fields(a.d, (uint32_t)bf) * F : bf;
+          if ((int)(key >> 48) != bf) key = kEmpty;  // a key outside its bag's field misses
+        }
+        const TabSel tb = pick_tab(a.d, key);
+        const uint32_t home = key == kEmpty ? 0u : home_slot(mix64(key), tb.n_home);
+        const uint32_t b = home / (uint32_t)kKeysPerBucket;
+        const uint32_t l0 = home - b * (uint32_t)kKeysPerBucket;
+        const uint32_t t = (a.d.n_tables == 2 && (key & 1ull)) ? 1u : 0u;
+        s_pk[w][lane] = key;
+        s_pb[w][lane] = b;
+        // bits 0-2 and 7: home lane in the bucket; bit 3: table; bits 8-31: buckets that may
+        // follow the home bucket (capped; far more than any probe sequence reaches)
+        s_pl[w][lane] = (l0 & 7u) | ((l0 & 8u) << 4) | (t << 3) |
+                        (min(tb.n_buckets - 1u - b, 0xFFFFFFu) << 8);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // round r: lane group g probes key (r0 + r) * 8 + g of the chunk.  All rounds' bucket
+      // loads are issued before any is evaluated; the few keys whose scan runs past their home
+      // bucket (about 3 % at load factor 0.5) then take further passes, again with every load
+      // issued first.
+      for (int r0 = 0; r0 < 64 / 8; r0 += kProbeRounds) {
+        int ext[kProbeRounds];  // buckets scanned past the home bucket; -1 once resolved
+#pragma unroll
+        for (int r = 0; r < kProbeRounds; ++r) ext[r] = 0;
+        bool more = true;
+        while (more) {
+          // staged values are re-read from LDS in each pass rather than held in registers
+          asm volatile("" ::: "memory");
+          u64x2 v[kProbeRounds];
+#pragma unroll
+          for (int r = 0; r < kProbeRounds; ++r) {
+            const int j = (r0 + r) * 8 + grp;
+            const uint32_t pl = s_pl[w][j];
+            const uint64_t b = (uint64_t)s_pb[w][j] + (uint64_t)(ext[r] > 0 ? ext[r] : 0);
+            const uint64_t* bp = a.d.tab[(pl >> 3) & 1u].buckets + b * kWordsPerBucket;
+            v[r] = *reinterpret_cast<const u64x2*>(bp + 2 * sub);
+          }
+          more = false;
+#pragma unroll
+          for (int r = 0; r < kProbeRounds; ++r) {
+            if (!__any(ext[r] >= 0)) continue;  // every group of this round is resolved
+            const int j = (r0 + r) * 8 + grp;
+            const uint64_t key = s_pk[w][j];
+            const uint32_t pl = s_pl[w][j];
+            const int l0 = ext[r] > 0 ? 0 : (int)(pl & 7u) + (int)((pl >> 4) & 8u);
+            const BucketHit h = eval_bucket<VAR>(a.d, v[r], key, l0, sub, grp);
+            if (ext[r] < 0) continue;
+            if (key == kEmpty || h.stop || (uint32_t)ext[r] >= (pl >> 8)) {
+              const int i = c0 + j;
+              if (sub == 0 && i < nk) {
+                const uint32_t rr = key == kEmpty ? kMiss : h.rr;
+                miss += (rr == kMiss);
+                if (in_lds) s_rr[i] = rr;
+                a.rowref[base + i] = rr;
+                if (a.slot) {
+                  const uint64_t b = (uint64_t)s_pb[w][j] + (uint64_t)ext[r];
+                  a.slot[base + i] = rr == kMiss ? -1 : (int64_t)(b * kKeysPerBucket) + h.l;
+                }
+              }
+              ext[r] = -1;
+            } else {
+              ext[r] += 1;
+              more = true;
+            }
+          }
+          more = __any(more);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+    }
   }
   if (miss) atomicAdd(&s_miss, miss);
   __syncthreads();
@@ -980,7 +1138,13 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
   const dim3 grid((a.n_bags + kFwdBags - 1) / kFwdBags);
   KTimer tm(ctx, "lookup_pool");
   const dim3 blk(kBlock);
-#define EMB_FWD(R, O, V) EMB_LAUNCH(tm, (k_lookup_pool<R, O, V>), grid, blk, 0, ctx.stream, a, gs)
+  // the probe form follows the size of the probed bucket array (see the two forms above)
+  const uint64_t bucket_bytes =
+      ((uint64_t)a.d.tab[0].n_buckets + (a.d.n_tables == 2 ? (uint64_t)a.d.tab[1].n_buckets : 0u)) *
+      kWordsPerBucket * 8u;
+  const bool coop = a.probe == 1 || (a.probe == 0 && bucket_bytes >= kCoopProbeBytes);
+#define EMB_FWD2(R, O, V, C) EMB_LAUNCH(tm, (k_lookup_pool<R, O, V, C>), grid, blk, 0, ctx.stream, a, gs)
+#define EMB_FWD(R, O, V) do { if (coop) EMB_FWD2(R, O, V, true); else EMB_FWD2(R, O, V, false); } while (0)
   if (a.d.row_f16) {
     if (a.out_f16) { if (a.d.var_dim) EMB_FWD(_Float16, _Float16, true); else EMB_FWD(_Float16, _Float16, false); }
     else { if (a.d.var_dim) EMB_FWD(_Float16, float, true); else EMB_FWD(_Float16, float, false); }
@@ -989,6 +1153,7 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
     else { if (a.d.var_dim) EMB_FWD(float, float, true); else EMB_FWD(float, float, false); }
   }
 #undef EMB_FWD
+#undef EMB_FWD2
   return hipGetLastError();
 }
 

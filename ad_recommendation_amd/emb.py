@@ -16,6 +16,8 @@ import numpy as np
 EMB_F32, EMB_F16 = 0, 1
 ROWREF_MISS = 0xFFFFFFFF
 FLAG_PINNED_STAGING = 1
+FLAG_PROBE_COOP = 2   # force the wave-cooperative bucket probe
+FLAG_PROBE_LANE = 4   # force the one-lane-per-key bucket probe
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmi355emb.so")

@@ -59,6 +59,11 @@ typedef enum {
 
 /* Table flags. */
 #define EMB_FLAG_PINNED_STAGING 1 /* keep the host image in pinned memory (needs a GPU at create) */
+/* The forward probes buckets either one lane per key or eight lanes per bucket (wave-cooperative);
+ * by default it picks the cooperative form for bucket arrays of 2 GiB and more, where the per-lane
+ * form's address translations thrash.  These flags force one form (both give the same results). */
+#define EMB_FLAG_PROBE_COOP 2
+#define EMB_FLAG_PROBE_LANE 4
 
 typedef struct {
   int32_t n_fields;          /* F, 1..65535; field id 0xFFFF is reserved for the EMPTY marker */

@@ -32,9 +32,9 @@ def _device():
     yield
 
 
-def gpu_table(w, keys, rows, master, dims):
+def gpu_table(w, keys, rows, master, dims, flags=0):
     T = emb.Table(dims, DT[w.row_dtype], w.has_master, w.n_tables, w.load_factor, w.acc_init,
-                  keys, rows, None, master)
+                  keys, rows, None, master, flags=flags)
     T.flash()
     return T
 
@@ -71,13 +71,13 @@ def gpu_step(T, keys, offsets, grad, out_dtype, grad_dtype, lr, eps, want_unique
     return res
 
 
-def run_parity(w, steps=3, batches=None, lr=None, eps=None, check_all_keys=True):
+def run_parity(w, steps=3, batches=None, lr=None, eps=None, check_all_keys=True, flags=0):
     """Run `steps` GPU steps and the oracle side by side; check every output."""
     dims = synth.field_dims(w)
     keys = synth.resident_keys(w)
     rows, master = synth.initial_state(w)
-    say(f"[parity] {w.name}: {keys.size} keys, building")
-    T = gpu_table(w, keys, rows, master, dims)
+    say(f"[parity] {w.name}: {keys.size} keys, building (flags {flags})")
+    T = gpu_table(w, keys, rows, master, dims, flags)
     ot = P.oracle_table(w, keys, rows, master, dims)
     bud = P.Budget(ot)
     lr = w.lr if lr is None else lr
@@ -181,6 +181,21 @@ def _edge_batches(w, keys, F):
 def test_edge_batches(w):
     keys = synth.resident_keys(w)
     run_parity(w, steps=2, batches=_edge_batches(w, keys, w.n_fields))
+
+
+@pytest.mark.parametrize("w", [W.TINY, W.scaled(W.F26, n_keys=1_000_000, batch=1024),
+                               W.scaled(W.F40_VARDIM, n_keys=1_000_000, batch=1024),
+                               W.scaled(W.F64_PASS, n_keys=1_000_000, batch=512)])
+def test_cooperative_probe(w):
+    # the wave-cooperative bucket probe (chosen by size for bucket arrays of 2 GiB and more),
+    # forced on tables small enough for the whole-table oracle, with the per-lane form's checks
+    run_parity(w, steps=2, check_all_keys=False, flags=emb.FLAG_PROBE_COOP)
+
+
+@pytest.mark.parametrize("w", [W.TINY, W.scaled(W.F40_VARDIM, n_keys=100_000, batch=16)])
+def test_cooperative_probe_edge_batches(w):
+    keys = synth.resident_keys(w)
+    run_parity(w, steps=2, batches=_edge_batches(w, keys, w.n_fields), flags=emb.FLAG_PROBE_COOP)
 
 
 def test_zero_gradient_leaves_rows_bit_identical():

@@ -5,13 +5,14 @@ in the launch configuration the benchmark times.
 The oracle cannot hold this table, so it checks samples it computes one by one:
   * slots and rowrefs of 20,000 sampled occurrences, bit-exact, from per-home key counts
     (``oracle.slots_of_sample``) rather than a sort of all 800M keys;
-  * the pooled output of 1 bag in 64, within the fp16 tolerance;
+  * the pooled output of 1 sample in 64 (all 64 of its bags), within the fp16 tolerance;
   * the number of distinct rows touched, bit-exact, and the count of sampled unique rows;
   * rows and accumulators of 1 % of the touched keys after the update, within the derived
     budgets, and sampled untouched keys bit-identical.
-For the pooled and update checks the oracle is a table over just the keys those samples need
-(every key of the sampled bags and every sampled touched key); keys outside it only act as
-misses there, which changes neither the sampled bags nor the sampled rows' gradients.
+For the pooled check the oracle is a table over the keys of the sampled samples, fed just those
+samples.  For the update check it is a table over the sampled touched keys, fed the batch with
+every other key's occurrences dropped (all bags and the full upstream gradient kept), which
+leaves those keys' gradient sums as they are.
 
 Opt-in (EMB_PASS_SCALE=1): building the table takes minutes and ~200 GB of host memory.
 """
@@ -57,25 +58,26 @@ def positions(keys, want, chunk=1 << 24):
 
 
 def initial_rows(w, pos, D):
-    """Initial rows of the resident keys at positions `pos` (fields regenerated one by one)."""
+    """Initial rows of the resident keys at positions `pos`: each field that holds one of them is
+    regenerated once (fields on a thread pool)."""
+    from concurrent.futures import ThreadPoolExecutor
     foff = synth.field_key_offsets(w)
     out = np.empty((pos.size, D), dtype=np.float16)
-    for f in range(w.n_fields):
+
+    def one(f):
         sel = np.nonzero((pos >= foff[f]) & (pos < foff[f + 1]))[0]
-        if sel.size == 0:
-            continue
-        r_f, _ = synth.field_state(w, f)
-        out[sel] = r_f.reshape(-1, D)[pos[sel] - foff[f]]
-    return out.reshape(-1)
+        if sel.size:
+            r_f, _ = synth.field_state(w, f)
+            out[sel] = r_f.reshape(-1, D)[pos[sel] - foff[f]]
+    with ThreadPoolExecutor(max(1, min(8, synth.worker_count()))) as ex:
+        list(ex.map(one, range(w.n_fields)))
+    return out
 
 
 def test_pass_scale_sampled_parity():
     import bench
     from tests.test_gpu_parity import gpu_step
     w = W.F64_PASS
-    dims = synth.field_dims(w)
-    D = int(dims[0])
-    F = w.n_fields
     t0 = time.perf_counter()
     T, keys, pinned = bench.build_table(w)
     say(f"table of {keys.size} keys built and filled in {time.perf_counter() - t0:.0f}s "
@@ -85,33 +87,56 @@ def test_pass_scale_sampled_parity():
     torch.cuda.synchronize()
     say(f"flashed in {time.perf_counter() - t0:.1f}s")
     bt = synth.batch(w, 0)
-    bkeys = bt["keys"].view(np.uint64)
-    nnz = bkeys.size
-    say(f"batch 0: {nnz} lookups")
+    say(f"batch 0: {bt['keys'].size} lookups")
     res = gpu_step(T, bt["keys"], bt["offsets"], bt["grad"], w.out_dtype, w.grad_dtype, w.lr,
                    w.eps)
     say(f"GPU step done: {res['n_unique']} unique rows, {res['n_miss']} misses")
     emb.pass_writeback(T.h)
     say("state written back")
-    assert res["n_miss"] == 0
+    check_sampled(w, keys, bt, res, T.export)
+    T.close()
 
+
+def check_sampled(w, keys, bt, res, export):
+    """The sampled checks on one step's results `res` (as gpu_step returns them) and the state
+    after it (`export(keys) -> rows, acc, master`)."""
+    dims = synth.field_dims(w)
+    D = int(dims[0])
+    F = w.n_fields
+    bkeys = bt["keys"].view(np.uint64)
+    nnz = bkeys.size
+    assert res["n_miss"] == 0
     r = np.random.default_rng(7)
     bk, bcount = np.unique(bkeys, return_counts=True)
     assert res["n_unique"] == bk.size
     uq = res["unique"].astype(np.int64)
     assert np.all(np.diff(uq) > 0)
-    # samples: occurrences (slots), 1 % of touched keys (counts, update), 1 bag in 64 (pooling)
+    # samples: occurrences (slots), 1 % of touched keys (counts, update), 1 sample in 64 with
+    # all of its bags (pooling)
     occ = np.unique(r.integers(0, nnz, size=20_000))
     pick = np.unique(r.integers(0, bk.size, size=max(1, bk.size // 100)))
     pick_keys = bk[pick]
-    bags = np.arange(0, bt["offsets"].size - 1, 64)
     off64 = bt["offsets"].astype(np.int64)
-    bag_occ = np.concatenate([np.arange(off64[j], off64[j + 1]) for j in bags])
-    need = np.unique(np.concatenate([bkeys[bag_occ], pick_keys]))
-    want = np.unique(np.concatenate([bkeys[occ], need]))
+    lens = np.diff(off64)
+    samp = np.arange(0, w.batch, 64)
+    bag_ids = (samp[:, None] * F + np.arange(F)[None, :]).reshape(-1)
+    sl = lens[bag_ids]
+    sub_off = np.concatenate([[0], np.cumsum(sl)])
+    sub_idx = np.repeat(off64[bag_ids], sl) + (np.arange(sub_off[-1]) - np.repeat(sub_off[:-1], sl))
+    sub_keys = bkeys[sub_idx]
+    fwd_keys = np.unique(sub_keys)
+    want = np.unique(np.concatenate([bkeys[occ], pick_keys, fwd_keys]))
     t0 = time.perf_counter()
     wpos = positions(keys, want)
     say(f"{want.size} sampled keys located in {time.perf_counter() - t0:.0f}s")
+    upos = np.unique(r.integers(0, keys.size, size=5000))      # untouched candidates
+    upos = upos[~np.isin(keys[upos], bk)]
+    t0 = time.perf_counter()
+    init = initial_rows(w, np.concatenate([wpos, upos]), D)
+    init_want, init_u = init[:wpos.size], init[wpos.size:]
+    del init
+    say(f"initial rows of {wpos.size + upos.size} keys regenerated in "
+        f"{time.perf_counter() - t0:.0f}s")
 
     # ---- slots and rowrefs, bit-exact (one row per granule: rowref = rank in slot order)
     nh = O.n_home_slots(keys.size, w.load_factor)
@@ -128,29 +153,35 @@ def test_pass_scale_sampled_parity():
     assert np.array_equal(res["count"][u_at], bcount[pick])
     say(f"{occ.size} slots, {pick.size} unique rows and counts match")
 
-    # ---- oracle over the keys the samples need
-    npos = wpos[np.searchsorted(want, need)]
-    ot = O.Table(need, dims, w.row_dtype, w.has_master, 1, w.load_factor, w.acc_init,
-                 initial_rows(w, npos, D))
-    say(f"oracle table over {need.size} keys")
-    pooled, _ = ot.forward(bt["keys"], bt["offsets"], w.out_dtype, bags=bags)
-    S = P.pooled_scale(ot, bt["keys"], bt["offsets"])
-    for j, v in pooled.items():
-        b, f = divmod(j, F)
-        P.check_pooled(res["out"][b, f * D:(f + 1) * D][None, :], v[None, :],
-                       S[b, f * D:(f + 1) * D][None, :], w.out_dtype)
-    say(f"{len(pooled)} sampled bags pooled within tolerance")
-    del S
+    # ---- pooled output of the sampled samples: the oracle over just their keys
+    ot = O.Table(fwd_keys, dims, w.row_dtype, w.has_master, 1, w.load_factor, w.acc_init,
+                 init_want[np.searchsorted(want, fwd_keys)].reshape(-1))
+    say(f"oracle table over {fwd_keys.size} keys of the sampled samples")
+    out_o, miss_o = ot.forward(sub_keys.view(np.int64), sub_off, w.out_dtype)
+    assert miss_o == 0
+    P.check_pooled(res["out"][samp], out_o, P.pooled_scale(ot, sub_keys.view(np.int64), sub_off),
+                   w.out_dtype)
+    say(f"{samp.size} sampled samples ({bag_ids.size} bags) pooled within tolerance")
+    del ot
 
+    # ---- update of the sampled touched keys: the batch restricted to their occurrences (every
+    # bag kept, other keys dropped) gives them the same gradient sums
+    m = np.isin(bkeys, pick_keys)
+    bag_of = np.repeat(np.arange(lens.size, dtype=np.int64), lens)
+    upd_off = np.concatenate([[0], np.cumsum(np.bincount(bag_of[m], minlength=lens.size))])
+    upd_keys = bkeys[m].view(np.int64)
+    del bag_of
+    ot = O.Table(pick_keys, dims, w.row_dtype, w.has_master, 1, w.load_factor, w.acc_init,
+                 init_want[np.searchsorted(want, pick_keys)].reshape(-1))
     bud = P.Budget(ot)
-    bud.oracle_step(ot, bt["keys"], bt["offsets"], bt["grad"], w.lr, w.eps)
-    rows_g, acc_g, _ = T.export(pick_keys)
+    t0 = time.perf_counter()
+    bud.oracle_step(ot, upd_keys, upd_off, bt["grad"], w.lr, w.eps)
+    say(f"oracle update of {pick.size} rows over {upd_keys.size} occurrences in "
+        f"{time.perf_counter() - t0:.0f}s")
+    rows_g, acc_g, _ = export(pick_keys)
     P.check_state(ot, bud, pick_keys, rows_g, acc_g, None)
     # untouched resident keys: bit-identical to their initial state
-    upos = np.unique(r.integers(0, keys.size, size=5000))
-    upos = upos[~np.isin(keys[upos], bk)]
-    ru, au, _ = T.export(keys[upos])
+    ru, au, _ = export(keys[upos])
     assert np.all(au == np.float32(w.acc_init))
-    assert ru.tobytes() == initial_rows(w, upos, D).tobytes()
+    assert ru.tobytes() == init_u.tobytes()
     say(f"{pick.size} updated rows within budget; {upos.size} untouched rows bit-identical")
-    T.close()
