@@ -421,11 +421,11 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
 }
 
 // ---------------------------------------------------------------- backward: radix sort
-// Stable LSD radix sort of (rowref, bag) pairs.  Digits are up to 11 bits wide, chosen so the row
-// space needs as few passes as possible; occurrences that missed get a bin of their own after
-// every digit value, so they never widen the key and always sort last.
+// Stable LSD radix sort of (rowref, bag) pairs.  Digits are up to 9 bits wide (see plan_bwd), as
+// few passes as that allows for the row space; occurrences that missed get a bin of their own
+// after every digit value, so they never widen the key and always sort last.
 constexpr int kOffStage = 2048;               // bag offsets staged in LDS for the first pass
-constexpr int kMaxBins = (1 << 11) + 1;
+constexpr int kMaxBins = (1 << 9) + 1;
 constexpr uint32_t kMissKey = 0xFFFFFFFFu;    // sorted-key value of a missed occurrence
 
 struct SortArgs {
@@ -1161,12 +1161,15 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
   BwdPlan p{};
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.n = (int32_t)nnz;
-  // key bits of the largest rowref; fewest passes of at most 11 bits
+  // key bits of the largest rowref; fewest passes of at most 8 or 9 bits
   int keybits = 0;
   while (keybits < 32 && rowref_space > 1 && ((uint64_t)(rowref_space - 1) >> keybits) != 0) ++keybits;
   // digit width: each tile's per-bin work (count, scan, offsets) must stay small next to its
-  // per-item work, so wide digits only pay once tiles hold thousands of items
-  const int maxbits = nnz >= (4 << 20) ? 11 : 8;
+  // per-item work, and each digit's run of a tile must stay long enough to write in whole lines.
+  // Measured on MI355X with 4096-item tiles: 9-bit digits cost no more per pass than 8-bit ones,
+  // while 10-bit digits make a pass ~1.9x slower (a 30-bit key sorts faster in 4 passes of 8 bits
+  // than in 3 of 10).
+  const int maxbits = nnz >= (4 << 20) ? 9 : 8;
   p.passes = keybits <= maxbits ? 1 : (keybits + maxbits - 1) / maxbits;
   p.bits = (keybits + p.passes - 1) / p.passes;
   // tiles: enough of them to spread a small batch over every CU, large ones for large batches
@@ -1214,9 +1217,7 @@ static void launch_scatter_ipt(const SortArgs& s, int logb, dim3 grid, hipStream
   const dim3 blk(kBlock);
   switch (logb) {
     case 8: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 8>), grid, blk, 0, st, s); break;
-    case 9: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 9>), grid, blk, 0, st, s); break;
-    case 10: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 10>), grid, blk, 0, st, s); break;
-    default: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 11>), grid, blk, 0, st, s); break;
+    default: EMB_LAUNCH(tm, (k_sort_scatter<FIRST, IPT, 9>), grid, blk, 0, st, s); break;
   }
 }
 

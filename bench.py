@@ -88,7 +88,7 @@ def sort_plan(nnz, rowref_space):
     keybits = 0
     while keybits < 32 and rowref_space > 1 and ((rowref_space - 1) >> keybits) != 0:
         keybits += 1
-    maxbits = 11 if nnz >= (4 << 20) else 8
+    maxbits = 9 if nnz >= (4 << 20) else 8
     passes = 1 if keybits <= maxbits else (keybits + maxbits - 1) // maxbits
     bits = (keybits + passes - 1) // passes
     ipt = 16 if nnz >= (4 << 20) else 8 if nnz >= (1 << 20) else 4
