@@ -769,7 +769,11 @@ __device__ __forceinline__ RawState<RowT, EPL, MASTER> load_state(const UpdArgs&
 }
 
 // Element-wise Adagrad on one lane's elements: acc += g^2; w -= lr * g / (sqrt(acc) + eps).
-// fp16 rows with a master copy update the master and store its fp16 rounding as the row.
+// fp16 rows with a master copy update the master and store its fp16 rounding as the row.  The
+// square root and the reciprocal are the hardware's (v_sqrt_f32, v_rcp_f32, about 1 ulp each);
+// the correctly rounded forms cost ~35 instructions per element, which made them the largest
+// share of the update kernel's instructions.  The error they add to the step (a few ulp of the
+// step) is far inside the fp32 parity tolerance.
 template <typename RowT, int EPL, bool MASTER>
 __device__ __forceinline__ void apply_state(const UpdArgs& a, uint32_t r, int e0,
                                             typename F32V<EPL>::t g,
@@ -780,8 +784,8 @@ __device__ __forceinline__ void apply_state(const UpdArgs& a, uint32_t r, int e0
   const V acc = to_f32<float, EPL>(st.acc) + g * g;
   V den;
 #pragma unroll
-  for (int q = 0; q < EPL; ++q) den[q] = __builtin_sqrtf(acc[q]) + a.eps;
-  const V w = to_f32<WT, EPL>(st.w) - (a.lr * g) / den;
+  for (int q = 0; q < EPL; ++q) den[q] = __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(acc[q]) + a.eps);
+  const V w = to_f32<WT, EPL>(st.w) - (a.lr * g) * den;
   store_from_f32<float, EPL>(a.d.acc + e, acc);
   if (MASTER) store_from_f32<float, EPL>(a.d.master + e, w);
   store_from_f32<RowT, EPL>(reinterpret_cast<RowT*>(a.d.rows) + e, w);
@@ -802,61 +806,45 @@ __device__ __forceinline__ typename VecOf<GradT, EPL>::t grad_raw(const UpdArgs&
   return load_raw<GradT, EPL>(G + (ok ? (uint64_t)b * a.d.out_width + col : 0ull));
 }
 
-// Segmented inclusive scan of one round across the wave's lane groups.  Segments are runs of
-// equal keys, so key equality marks them; the carry adds the part of the first segment that lies
-// in earlier rounds.  Returns the segment sum so far; updates the carry (the last group's sum,
-// its key, and the index of its segment's first occurrence).
-template <int EPL>
-__device__ __forceinline__ typename F32V<EPL>::t seg_scan(int gs_log2, int64_t i, uint32_t kr,
-                                                          typename F32V<EPL>::t xr,
-                                                          uint32_t& carry_key,
-                                                          typename F32V<EPL>::t& carry,
-                                                          int64_t& carry_head) {
-  typedef typename F32V<EPL>::t V;
-  const int GS = 1 << gs_log2;
-  const int IPR = 64 >> gs_log2;
-  const int lane = lane_id();
-  const int li = lane & (GS - 1);
-  const int g = lane >> gs_log2;
-  for (int d = 1; d < IPR; d <<= 1) {
-    V y;
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) y[q] = __shfl_up(xr[q], d * GS, 64);
-    const uint32_t ky = __shfl_up(kr, d * GS, 64);
-    if (g >= d && ky == kr) xr += y;
-  }
-  if (kr == carry_key) xr += carry;
-  const int src = (IPR - 1) * GS + li;
-  V nc;
-#pragma unroll
-  for (int q = 0; q < EPL; ++q) nc[q] = __shfl(xr[q], src, 64);
-  const uint32_t nk = __shfl(kr, src, 64);
-  if (nk != carry_key) {
-    const uint64_t m = __ballot(kr == nk);
-    const int first = m ? (__builtin_ctzll(m) >> gs_log2) : 0;
-    carry_head = i - g + first;
-  }
-  carry = nc;
-  carry_key = nk;
-  return xr;
-}
-
 template <int EPL> struct SegBatch { static constexpr int value = EPL == 4 ? 4 : 2; };
 
 constexpr uint32_t kHeadEnds = 1u, kHeadPasses = 2u;
 
 constexpr int kPieceMax = 256;  // occurrences per update piece, at most
 
-// Segmented gradient reduction in sorted order fused with the Adagrad update.  Each wave owns
-// pieces of `rounds` x (64/GS) consecutive sorted occurrences (lane group g of a round holds one
-// occurrence).  The piece's sorted keys (with one neighbour on each side) and bags are first
-// staged in the wave's LDS region with coalesced loads.  A segmented scan across the groups, with
-// a carry between rounds, then sums each row's occurrences in order.  A segment that begins and
-// ends inside the piece is applied at its last occurrence.  The piece's first segment, when it
-// began in an earlier piece, is left as a head partial; its last segment, when it runs into the
-// next piece, as a tail partial; k_update_fixup joins them.  Each batch of rounds issues its
-// gradient-slice loads together with the state of the rows that end in the batch.  The kernel is
-// held to 128 VGPRs (four waves per SIMD instead of three) at the cost of a few spilled values.
+// Carries of the segments that cross lane-group boundaries inside a piece, combined once per
+// piece: group g contributes (reset, v, valid) where reset means the carry it passes on does not
+// include what reached it.  Inclusive segmented scan over the wave's groups (stride GS lanes).
+template <int EPL>
+__device__ __forceinline__ void group_scan(int gs_log2, int g, bool& reset,
+                                           typename F32V<EPL>::t& v, bool& valid) {
+  typedef typename F32V<EPL>::t V;
+  const int GS = 1 << gs_log2;
+  const int IPR = 64 >> gs_log2;
+  for (int d = 1; d < IPR; d <<= 1) {
+    V y;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) y[q] = __shfl_up(v[q], d * GS, 64);
+    const int rv = __shfl_up((int)reset | ((int)valid << 1), d * GS, 64);
+    if (g >= d && !reset) {
+      v += y;
+      valid = (rv >> 1) & 1;
+      reset = rv & 1;
+    }
+  }
+}
+
+// Segmented gradient reduction in sorted order fused with the Adagrad update.  A wave owns pieces
+// of IPR x K consecutive sorted occurrences (IPR = 64 / GS lane groups of GS lanes; `rounds` is
+// K); lane group g takes the piece's occurrences g*K .. g*K+K-1 and sums them one after another,
+// restarting at each segment head (segments are runs of equal rows).  A segment that begins and
+// ends inside one group is applied there, its state loads issued with the gradient loads of the
+// batch that ends it.  The segments that cross group boundaries are joined once per piece by a
+// segmented scan over the groups; those that end inside the piece are applied by the group where
+// they end.  The piece's first segment, when it began in an earlier piece, is left as a head
+// partial, and its last segment, when it runs into the next piece, as a tail partial;
+// k_update_fixup joins them.  The piece's sorted keys (with one neighbour on each side) and bags
+// are staged in the wave's LDS region first, with coalesced loads.
 template <typename RowT, typename GradT, bool VAR, bool MASTER>
 __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
@@ -870,7 +858,8 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
   __syncthreads();
   const int GS = 1 << gs_log2;
   const int IPR = 64 >> gs_log2;
-  const int PW = a.rounds * IPR;
+  const int K = a.rounds;
+  const int PW = K * IPR;
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
   const int li = lane & (GS - 1);
@@ -904,63 +893,106 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const uint32_t k0 = sk[1];
-    // the piece's first segment began in an earlier piece
-    const bool cont = k0 < a.miss_key && sk[0] == k0;
-    uint32_t carry_key = NONE;
-    V carry = 0.0f;
-    int64_t carry_head = -1;
-    int carry_D = 0;
-    bool head_ended = false;
-    for (int rb = 0; rb < a.rounds; rb += BR) {
-      uint32_t k[BR];
-      bool hd[BR], upd[BR], cend[BR], okg[BR];
+    // sk[j + 1] is the key of piece position j
+    const int j0 = g * K;
+    const uint32_t kfirst = sk[j0 + 1];
+    // the group's first segment began before the group
+    const bool gcont = kfirst < a.miss_key && sk[j0] == kfirst;
+    V s = 0.0f;          // running sum of the current segment
+    V hsum = 0.0f;       // the group's first segment, when it began earlier and ends in the group
+    bool hends = false;
+    int gD = 0;          // row width of the group's first occurrence
+    for (int k0 = 0; k0 < K; k0 += BR) {
+      uint32_t kk[BR];
+      bool hd[BR], upd[BR], hend[BR], okg[BR];
       typename VecOf<GradT, EPL>::t gr[BR];
       RawState<RowT, EPL, MASTER> st[BR];
       int D[BR];
       // issue every load of the batch: gradient slices and the state of rows ending here
 #pragma unroll
       for (int r = 0; r < BR; ++r) {
-        const int j = (rb + r) * IPR + g;
-        const uint32_t kk = sk[j + 1];
-        const uint32_t kp = sk[j];
-        const uint32_t kn = sk[j + 2];
-        const bool own = kk < a.miss_key;
-        k[r] = own ? kk : NONE;
-        hd[r] = own && kp != kk;
-        const bool end = own && kn != kk;
-        const bool is_cont = own && cont && kk == k0;
+        const int j = j0 + k0 + r;
+        const uint32_t kr = sk[j + 1];
+        const bool own = kr < a.miss_key;
+        const bool in_grp = own && !(gcont && kr == kfirst);
+        const bool end = own && sk[j + 2] != kr;
+        kk[r] = own ? kr : NONE;
+        hd[r] = own && sk[j] != kr;
         gr[r] = grad_raw<GradT, EPL, VAR>(a, sv[j], e0, own, D[r], okg[r]);
-        upd[r] = end && !is_cont && okg[r];
-        cend[r] = end && is_cont;
-        st[r] = load_state<RowT, EPL, MASTER>(a, k[r], e0, upd[r]);
+        upd[r] = end && in_grp && okg[r];
+        hend[r] = end && !in_grp;
+        st[r] = load_state<RowT, EPL, MASTER>(a, kk[r], e0, upd[r]);
       }
+      if (k0 == 0) gD = D[0];
 #pragma unroll
       for (int r = 0; r < BR; ++r) {
-        const int64_t i = p0 + (int64_t)(rb + r) * IPR + g;
-        const uint32_t prev_carry = carry_key;
         const V x = okg[r] ? to_f32<GradT, EPL>(gr[r]) : V(0.0f);
-        const V sum = seg_scan<EPL>(gs_log2, i, k[r], x, carry_key, carry, carry_head);
-        if (carry_key != prev_carry) carry_D = __shfl(D[r], (IPR - 1) * GS, 64);
-        if (hd[r]) heads += (li == 0);
-        if (upd[r]) apply_state<RowT, EPL, MASTER>(a, k[r], e0, sum, st[r]);
-        if (cend[r] && e0 < D[r]) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, sum);
-        head_ended = head_ended || (__ballot(cend[r]) != 0);
+        s = hd[r] ? x : s + x;
+        heads += (hd[r] && li == 0) ? 1u : 0u;
+        if (upd[r]) apply_state<RowT, EPL, MASTER>(a, kk[r], e0, s, st[r]);
+        if (hend[r]) {
+          hsum = s;
+          hends = true;
+        }
       }
     }
-    // the last segment runs into the next piece: leave its sum for the fixup
-    uint32_t flag = head_ended ? (kHeadEnds << 1) : 0u;
-    if (carry_key < a.miss_key && sk[PW + 1] == carry_key) {
-      if (cont && carry_key == k0) {
-        flag |= kHeadPasses << 1;  // the first segment spans the whole piece
-        if (g == 0 && e0 < carry_D) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, carry);
-      } else {
-        flag |= 1u;
-        if (g == 0 && e0 < carry_D) store_from_f32<float, EPL>(a.ptail + c * a.pdim + e0, carry);
-        if (lane == 0) {
-          a.pkey[2 * c] = carry_key;
-          a.pkey[2 * c + 1] = (uint32_t)carry_D;
-        }
+    // what this group passes on: its last segment when that runs past the group's end
+    const uint32_t klast = sk[j0 + K];
+    const bool lown = klast < a.miss_key;
+    const bool lcont = lown && sk[j0 + K + 1] == klast;       // runs past the group's end
+    const bool passes = gcont && !hends && lown && klast == kfirst && lcont;
+    const bool tf = lcont && !passes;                          // began inside the group
+    // group scan: reset unless the group passes its carry through; the carry is then the
+    // group's sum (its whole range) added to what reached it, else its tail sum
+    bool reset = !passes;
+    V v = (passes || tf) ? s : V(0.0f);
+    bool valid = tf;
+    group_scan<EPL>(gs_log2, g, reset, v, valid);
+    // carry reaching group g: the inclusive value of group g - 1; group 0 receives the piece's
+    // head chain (nothing summed yet here, valid when the piece begins inside a segment)
+    const bool cont = sk[1] < a.miss_key && sk[0] == sk[1];
+    V cin;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) cin[q] = __shfl_up(v[q], GS, 64);
+    const int rvin = __shfl_up((int)reset | ((int)valid << 1), GS, 64);
+    if (g == 0) cin = 0.0f;
+    // head partial ending in this group: the piece's first segment (begun in an earlier piece,
+    // passed through every group before this one) or a row begun in an earlier group
+    uint32_t flag = 0;
+    const bool chain_ends = gcont && hends;
+    const bool piece_head_ends = chain_ends && cont && (g == 0 || !(rvin & 1));
+    const bool row_ends = chain_ends && !piece_head_ends;
+    const V total = cin + hsum;
+    const RawState<RowT, EPL, MASTER> sth =
+        load_state<RowT, EPL, MASTER>(a, kfirst, e0, row_ends && e0 < gD);
+    if (row_ends && e0 < gD) apply_state<RowT, EPL, MASTER>(a, kfirst, e0, total, sth);
+    if (piece_head_ends && e0 < gD) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, total);
+    if (__ballot(piece_head_ends) != 0) flag |= kHeadEnds << 1;
+    // the last group's carry runs into the next piece
+    const int src = (IPR - 1) * GS + li;
+    V cl;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) cl[q] = __shfl(v[q], src, 64);
+    const int rvl = __shfl((int)reset | ((int)valid << 1), src, 64);
+    const uint32_t kl = __shfl(klast, src, 64);
+    // valid at the last group: its tail, or a pass-through chain that began at a tail (valid) or
+    // at the piece's head (no reset anywhere and the piece began inside a segment)
+    const bool l_reset = rvl & 1, l_valid = (rvl >> 1) & 1;
+    const bool whole_piece = !l_reset && cont;  // one segment across the whole piece
+    if (whole_piece) {
+      flag |= kHeadPasses << 1;
+      if (g == 0 && e0 < gD) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, cl);
+    } else if (l_valid) {
+      flag |= 1u;
+      // row width of the tail's row: that of the last group's last occurrence
+      int Dl;
+      bool okl;
+      const uint32_t bag_l = sv[min((IPR - 1) * K + K - 1, PW - 1)];
+      (void)grad_raw<GradT, EPL, VAR>(a, bag_l, e0, false, Dl, okl);
+      if (g == 0 && e0 < Dl) store_from_f32<float, EPL>(a.ptail + c * a.pdim + e0, cl);
+      if (lane == 0) {
+        a.pkey[2 * c] = kl;
+        a.pkey[2 * c + 1] = (uint32_t)Dl;
       }
     }
     if (lane == 0) a.pflag[c] = flag;
@@ -1173,7 +1205,7 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
   p.passes = keybits <= maxbits ? 1 : (keybits + maxbits - 1) / maxbits;
   p.bits = (keybits + p.passes - 1) / p.passes;
   // tiles: enough of them to spread a small batch over every CU, large ones for large batches
-  p.ipt = nnz >= (4 << 20) ? 16 : nnz >= (1 << 20) ? 8 : 4;
+  p.ipt = nnz >= (1 << 20) ? 8 : 4;
   const int64_t tile = (int64_t)kBlock * p.ipt;
   p.tiles = (int32_t)((nnz + tile - 1) / tile);
   const size_t n = (size_t)(nnz > 0 ? nnz : 0);
@@ -1197,7 +1229,7 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
   const int ipr = 64 >> p.gsl;
   const int br = row_f16 ? SegBatch<8>::value : SegBatch<4>::value;
   int64_t r = (nnz + (int64_t)ipr * 131072 - 1) / ((int64_t)ipr * 131072);
-  const int64_t rmax = kPieceMax / ipr < 16 ? kPieceMax / ipr : 16;
+  const int64_t rmax = kPieceMax / ipr;
   r = r < br ? br : r > rmax ? rmax : r;
   p.rounds = (int32_t)((r + br - 1) / br * br);
   const int64_t pw = (int64_t)p.rounds * ipr;
@@ -1223,12 +1255,8 @@ static void launch_scatter_ipt(const SortArgs& s, int logb, dim3 grid, hipStream
 
 template <bool FIRST>
 static void launch_scatter(const SortArgs& s, int ipt, int logb, dim3 grid, hipStream_t st, KTimer& tm) {
-  switch (ipt) {
-    case 2: launch_scatter_ipt<FIRST, 2>(s, logb, grid, st, tm); break;
-    case 4: launch_scatter_ipt<FIRST, 4>(s, logb, grid, st, tm); break;
-    case 8: launch_scatter_ipt<FIRST, 8>(s, logb, grid, st, tm); break;
-    default: launch_scatter_ipt<FIRST, 16>(s, logb, grid, st, tm); break;
-  }
+  if (ipt == 4) launch_scatter_ipt<FIRST, 4>(s, logb, grid, st, tm);
+  else launch_scatter_ipt<FIRST, 8>(s, logb, grid, st, tm);
 }
 
 hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ctx) {

@@ -49,7 +49,7 @@ def piece_plan(nnz, max_dim, row_f16):
     ipr = 64 >> gsl
     br = 2 if row_f16 else 4
     r = (nnz + ipr * 131072 - 1) // (ipr * 131072)
-    r = min(max(r, br), min(16, 256 // ipr))
+    r = min(max(r, br), 256 // ipr)
     rounds = (r + br - 1) // br * br
     return rounds * ipr, (nnz + rounds * ipr - 1) // (rounds * ipr)
 
@@ -91,7 +91,7 @@ def sort_plan(nnz, rowref_space):
     maxbits = 9 if nnz >= (4 << 20) else 8
     passes = 1 if keybits <= maxbits else (keybits + maxbits - 1) // maxbits
     bits = (keybits + passes - 1) // passes
-    ipt = 16 if nnz >= (4 << 20) else 8 if nnz >= (1 << 20) else 4
+    ipt = 8 if nnz >= (1 << 20) else 4
     return ipt, (nnz + 256 * ipt - 1) // (256 * ipt), bits
 
 
