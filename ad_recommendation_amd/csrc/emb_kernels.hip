@@ -264,6 +264,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   constexpr int EPL = 16 / (int)sizeof(RowT);
   typedef typename F32V<EPL>::t AccV;
   __shared__ int32_t s_off[kFwdBags + 1];
+  __shared__ int32_t s_lane0[kFwdBags + 1];       // mixed widths: first packed lane of each bag
   __shared__ uint32_t s_rr[kFwdKeyCap];
   __shared__ uint64_t s_pk[kWaves][64];          // keys of the wave's chunk (EMPTY: no probe)
   __shared__ uint32_t s_pb[kWaves][64];          // their home buckets
@@ -398,10 +399,47 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   __syncthreads();
   if (tid == 0 && s_miss && a.n_miss) atomicAdd(a.n_miss, (unsigned long long)s_miss);
 
+  OutT* out = reinterpret_cast<OutT*>(a.out);
+  if (VAR) {
+    // phase 2, mixed widths: bag jb takes D/EPL consecutive lanes of a packed lane space (no
+    // lane idles on a narrow field), EPL elements per lane
+    if (tid < 64) {
+      int L = 0;
+      if (tid < nb) {
+        int f = f0 + tid;
+        f = f >= F ? f - (int)div_fields(a.d, (uint32_t)f) * F : f;
+        L = a.d.fdim[f] / EPL;
+      }
+      const uint32_t incl = wave_incl_scan((uint32_t)L);
+      s_lane0[tid] = (int)incl - L;
+      if (tid == 63) s_lane0[64] = (int)incl;
+    }
+    __syncthreads();
+    const int lanes = s_lane0[64];
+    for (int v = tid; v < lanes; v += kBlock) {
+      int lo = 0, hi = nb - 1;  // the bag whose lane range holds v
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_lane0[mid] <= v) lo = mid; else hi = mid - 1;
+      }
+      const int jb = lo;
+      int f = f0 + jb;
+      f = f >= F ? f - (int)div_fields(a.d, (uint32_t)f) * F : f;
+      const int e0 = (v - s_lane0[jb]) * EPL;
+      const uint32_t b = div_fields(a.d, (uint32_t)(j0 + jb));
+      const int k0 = min(max(s_off[jb] - base, 0), nk), k1 = min(max(s_off[jb + 1] - base, k0), nk);
+      AccV acc;
+      if (in_lds)
+        acc = pool_rows<RowT>(a.d, [&](int k) { return s_rr[k]; }, k0, k1, e0);
+      else
+        acc = pool_rows<RowT>(a.d, [&](int k) { return a.rowref[base + k]; }, k0, k1, e0);
+      store_from_f32<OutT, EPL>(out + (uint64_t)b * a.d.out_width + a.d.fcol[f] + e0, acc);
+    }
+    return;
+  }
   // phase 2: a group of 2^gs_log2 lanes per bag, EPL elements per lane
   const int lane = tid & ((1 << gs_log2) - 1);
   const int ngrp = kBlock >> gs_log2;
-  OutT* out = reinterpret_cast<OutT*>(a.out);
   const int e0 = lane * EPL;
   for (int jb = tid >> gs_log2; jb < nb; jb += ngrp) {
     int f = f0 + jb;
