@@ -188,6 +188,8 @@ struct EmbTable {
   double lf = 0.5;
   float acc_init = 0.f;
   int32_t granule = 1, var_dim = 0, max_dim = 0, out_width = 0;
+  std::vector<int32_t> gsl;          // per field: log2 of the lanes (16-byte slices) of its rows
+  int32_t classed = 0, cls_shift = 0;
   size_t elem_bytes = 4;
   // layout
   struct Sub {
@@ -243,6 +245,9 @@ struct EmbTable {
     d.fdim = meta;
     d.fcol = meta + F;
     d.fgran = meta + 2 * F;
+    d.fgsl = meta + 3 * F;
+    d.classed = classed;
+    d.cls_shift = cls_shift;
     d.rowref_space = rowref_space;
     // division by the field count as a multiply and shift (exact for dividends below 2^31)
     int l = 0;
@@ -512,6 +517,27 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
     if (rr_total >= 0xFFFFFFFFull) return fail(EMB_ERANGE, "rowref space exceeds 32 bits");
   }
   T->rowref_space = (uint32_t)rr_total;
+  // width classes: log2 of the 16-byte lanes a row takes; the backward sorts mixed-width tables
+  // by (class, rowref) when the classes fit above the rowref bits and the first radix digit
+  // (at most 9 bits) stays below them
+  {
+    const int epl = T->row_dtype == EMB_F16 ? 8 : 4;
+    int cmin = 99, cmax = -1;
+    for (int f = 0; f < T->F; ++f) {
+      const int lanes = (T->dim[f] + epl - 1) / epl;
+      int g = 0;
+      while ((1 << g) < lanes) ++g;
+      T->gsl.push_back(g);
+      cmin = std::min(cmin, g);
+      cmax = std::max(cmax, g);
+    }
+    int rbits = 0;
+    while (rbits < 32 && T->rowref_space > 1 && ((uint64_t)(T->rowref_space - 1) >> rbits) != 0) ++rbits;
+    if (cmax > cmin && rbits >= 9 && rbits + 3 <= 31) {
+      T->classed = 1;
+      T->cls_shift = rbits;
+    }
+  }
   T->mean_disp = N ? disp_sum / (double)N : 0.0;
 
   // image layout = arena layout
@@ -523,7 +549,7 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
   T->off_meta = align256(T->off_master + (T->has_master ? T->total_elems * 4 : 0));
   // 4 KiB of tail padding: kernels read row 0 (+ lane offset) in place of a masked-off row, which
   // must stay inside the arena even for an empty table
-  T->arena_bytes = align256(T->off_meta + 3 * 4 * (size_t)T->F) + 4096;
+  T->arena_bytes = align256(T->off_meta + 4 * 4 * (size_t)T->F) + 4096;
   if (T->flags & EMB_FLAG_PINNED_STAGING) {
     hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&T->image), T->arena_bytes, 0);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the host image");
@@ -605,6 +631,7 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
     meta[f] = T->dim[f];
     meta[T->F + f] = T->col[f];
     meta[2 * T->F + f] = T->gran[f];
+    meta[3 * T->F + f] = T->gsl[f];
   }
   *out = guard.release();
   return EMB_OK;
@@ -627,6 +654,7 @@ int table_info(const EmbTable* t, EmbTableInfo* info) {
   }
   info->mean_displacement = t->mean_disp;
   info->max_displacement = t->max_disp;
+  info->unique_by_width = (uint32_t)t->classed;
   return EMB_OK;
 }
 
@@ -687,7 +715,7 @@ int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets
 int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* bytes) {
   if (!t || !bytes) return fail(EMB_EINVAL, "null argument");
   if (n_bags < 0 || nnz < 0 || nnz >= (1ll << 31)) return fail(EMB_EINVAL, "bad sizes");
-  *bytes = plan_bwd(nnz, t->rowref_space, t->max_dim, t->row_dtype == EMB_F16).bytes;
+  *bytes = plan_bwd(nnz, t->rowref_space, t->max_dim, t->row_dtype == EMB_F16, t->classed).bytes;
   return EMB_OK;
 }
 
@@ -707,7 +735,7 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
   if ((reinterpret_cast<uintptr_t>(d_grad) | reinterpret_cast<uintptr_t>(d_rowref) |
        reinterpret_cast<uintptr_t>(d_ws)) % 16)
     return fail(EMB_EINVAL, "d_grad, d_rowref and d_ws must be 16-byte aligned");
-  const BwdPlan p = plan_bwd(nnz, t->rowref_space, t->max_dim, t->row_dtype == EMB_F16);
+  const BwdPlan p = plan_bwd(nnz, t->rowref_space, t->max_dim, t->row_dtype == EMB_F16, t->classed);
   if (nnz > 0 && ws_bytes < p.bytes) return fail(EMB_ENOSPACE, "workspace smaller than bwd_workspace_bytes()");
   if (!t->flashed) return fail(EMB_ESTATE, "backward before pass_flash");
   BwdLaunch a{};

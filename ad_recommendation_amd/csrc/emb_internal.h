@@ -57,6 +57,11 @@ struct DevDesc {
   uint32_t rowref_space; // rowref values are < rowref_space
   uint32_t fdiv_m;       // n / n_fields == (n * fdiv_m) >> fdiv_s for every n < 2^31
   int32_t fdiv_s;
+  // Width classes (mixed-width tables): the backward sorts by (class, rowref), the class being
+  // log2 of the lanes a row of the field takes, so that each update piece sees one row width.
+  int32_t classed;       // 1: sort keys carry the class above bit cls_shift
+  int32_t cls_shift;     // bits of the rowref part of a sort key
+  const int32_t* fgsl;   // [F] class (log2 lanes per row) of each field
 };
 
 // Kernel timing: events bracket each launch when enabled.
@@ -122,7 +127,8 @@ struct BwdPlan {
   int32_t passes;      // radix passes
   int32_t bits;        // digit bits per pass (<= 11); one extra bin holds misses
   int32_t gsl;         // log2 lanes per row in the update kernels
-  int32_t rounds;      // rounds per update piece
+  int32_t rounds;      // occurrences per lane group in an update piece (widest rows)
+  int32_t pw;          // occurrences per update piece
   int32_t n_pieces;    // update pieces
   int32_t pdim;        // floats per partial
   int32_t groups;      // histogram groups of tiles
@@ -131,7 +137,9 @@ struct BwdPlan {
   size_t off_phead, off_ptail, off_pflag, off_pkey;
   size_t bytes;
 };
-BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t row_f16);
+// `classed`: sort keys carry a 3-bit width class above the rowref bits (DevDesc::classed).
+BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t row_f16,
+                 int32_t classed);
 
 // Launchers (emb_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx);

@@ -486,6 +486,13 @@ struct SortArgs {
   uint32_t rowref_space;
   int32_t shift;
   int32_t bits;       // digit bits of this pass; bin (1 << bits) holds the misses
+  // width classes of mixed-width tables (the first pass puts them above the rowref bits)
+  int32_t classed;
+  int32_t cls_shift;
+  const int32_t* fgsl;
+  int32_t n_fields;
+  uint32_t fdiv_m;
+  int32_t fdiv_s;
 };
 
 __device__ __forceinline__ uint32_t sort_key_of(uint32_t rr, uint32_t space) {
@@ -710,6 +717,10 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
         } else {
           vv = (uint32_t)bag_search_global(a.offsets, jlo, a.n_bags - 1, i);
         }
+        if (a.classed && kk != kMissKey) {
+          const uint32_t b = (uint32_t)(((uint64_t)vv * a.fdiv_m) >> a.fdiv_s);
+          kk |= (uint32_t)a.fgsl[vv - b * (uint32_t)a.n_fields] << a.cls_shift;
+        }
       } else {
         kk = key[k];
         vv = val[k];
@@ -776,6 +787,7 @@ struct UpdArgs {
   int64_t* n_unique;
   // pieces: each wave reduces `rounds` x (64 / GS) consecutive sorted occurrences
   int32_t rounds;
+  int32_t pw;            // occurrences per piece
   int32_t n_pieces;
   int32_t pdim;          // floats per partial (widest row)
   float* phead;          // [n_pieces][pdim] sum of the piece's first segment when it began earlier
@@ -894,16 +906,12 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
   __shared__ uint32_t s_val[kWaves][kPieceMax];
   if (threadIdx.x == 0) s_heads = 0;
   __syncthreads();
-  const int GS = 1 << gs_log2;
-  const int IPR = 64 >> gs_log2;
-  const int K = a.rounds;
-  const int PW = K * IPR;
+  const int PW = a.pw;
   const int lane = lane_id();
   const int wv = threadIdx.x >> 6;
-  const int li = lane & (GS - 1);
-  const int g = lane >> gs_log2;
-  const int e0 = li * EPL;
   const uint32_t NONE = 0xFFFFFFFFu;  // above every row key; equal to the miss key
+  // rowref part of a sort key (mixed-width tables carry the width class above it)
+  const uint32_t rmask = a.d.classed ? (1u << a.d.cls_shift) - 1u : 0xFFFFFFFFu;
   uint32_t* sk = s_key[wv];
   uint32_t* sv = s_val[wv];
   const int64_t wstride = (int64_t)gridDim.x * (kBlock / 64);
@@ -931,6 +939,16 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // lane groups: as wide as the piece's widest rows (its last key's width class, the classes
+    // being sorted above the rowrefs), else the table's widest
+    int gsl = gs_log2;
+    if (a.d.classed && sk[PW] < a.miss_key) gsl = (int)(sk[PW] >> a.d.cls_shift);
+    const int GS = 1 << gsl;
+    const int IPR = 64 >> gsl;
+    const int K = PW / IPR;
+    const int li = lane & (GS - 1);
+    const int g = lane >> gsl;
+    const int e0 = li * EPL;
     // sk[j + 1] is the key of piece position j
     const int j0 = g * K;
     const uint32_t kfirst = sk[j0 + 1];
@@ -959,7 +977,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
         gr[r] = grad_raw<GradT, EPL, VAR>(a, sv[j], e0, own, D[r], okg[r]);
         upd[r] = end && in_grp && okg[r];
         hend[r] = end && !in_grp;
-        st[r] = load_state<RowT, EPL, MASTER>(a, kk[r], e0, upd[r]);
+        st[r] = load_state<RowT, EPL, MASTER>(a, kk[r] & rmask, e0, upd[r]);
       }
       if (k0 == 0) gD = D[0];
 #pragma unroll
@@ -967,7 +985,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
         const V x = okg[r] ? to_f32<GradT, EPL>(gr[r]) : V(0.0f);
         s = hd[r] ? x : s + x;
         heads += (hd[r] && li == 0) ? 1u : 0u;
-        if (upd[r]) apply_state<RowT, EPL, MASTER>(a, kk[r], e0, s, st[r]);
+        if (upd[r]) apply_state<RowT, EPL, MASTER>(a, kk[r] & rmask, e0, s, st[r]);
         if (hend[r]) {
           hsum = s;
           hends = true;
@@ -985,7 +1003,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
     bool reset = !passes;
     V v = (passes || tf) ? s : V(0.0f);
     bool valid = tf;
-    group_scan<EPL>(gs_log2, g, reset, v, valid);
+    group_scan<EPL>(gsl, g, reset, v, valid);
     // carry reaching group g: the inclusive value of group g - 1; group 0 receives the piece's
     // head chain (nothing summed yet here, valid when the piece begins inside a segment)
     const bool cont = sk[1] < a.miss_key && sk[0] == sk[1];
@@ -1002,8 +1020,8 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
     const bool row_ends = chain_ends && !piece_head_ends;
     const V total = cin + hsum;
     const RawState<RowT, EPL, MASTER> sth =
-        load_state<RowT, EPL, MASTER>(a, kfirst, e0, row_ends && e0 < gD);
-    if (row_ends && e0 < gD) apply_state<RowT, EPL, MASTER>(a, kfirst, e0, total, sth);
+        load_state<RowT, EPL, MASTER>(a, kfirst & rmask, e0, row_ends && e0 < gD);
+    if (row_ends && e0 < gD) apply_state<RowT, EPL, MASTER>(a, kfirst & rmask, e0, total, sth);
     if (piece_head_ends && e0 < gD) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, total);
     if (__ballot(piece_head_ends) != 0) flag |= kHeadEnds << 1;
     // the last group's carry runs into the next piece
@@ -1029,7 +1047,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
       (void)grad_raw<GradT, EPL, VAR>(a, bag_l, e0, false, Dl, okl);
       if (g == 0 && e0 < Dl) store_from_f32<float, EPL>(a.ptail + c * a.pdim + e0, cl);
       if (lane == 0) {
-        a.pkey[2 * c] = kl;
+        a.pkey[2 * c] = kl & rmask;
         a.pkey[2 * c + 1] = (uint32_t)Dl;
       }
     }
@@ -1037,8 +1055,9 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
   }
-  uint32_t wsum = 0;
-  for (int q = 0; q < 64; q += GS) wsum += __shfl(heads, q, 64);
+  // heads were counted by the first lane of each group, whatever the group width per piece
+  uint32_t wsum = heads;
+  for (int d = 32; d >= 1; d >>= 1) wsum += __shfl_xor(wsum, d, 64);
   if (lane == 0 && wsum) atomicAdd(&s_heads, wsum);
   __syncthreads();
   if (threadIdx.x == 0 && s_heads) atomicAdd(&a.ctr[1], s_heads);
@@ -1111,6 +1130,7 @@ struct SegArgs {
   uint32_t* unique;
   int32_t* count;
   uint32_t* nvalid;   // one word: number of non-miss occurrences
+  uint32_t rmask;     // rowref part of a sort key
 };
 
 __device__ __forceinline__ bool seg_head(const SegArgs& a, int32_t i) {
@@ -1161,7 +1181,7 @@ __global__ __launch_bounds__(kBlock) void k_seg_write(SegArgs a) {
     uint32_t total;
     const uint32_t pre = block_excl_scan(h ? 1u : 0u, s_w, total);
     if (h) {
-      a.unique[base + pre] = a.key[i];
+      a.unique[base + pre] = a.key[i] & a.rmask;
       a.headpos[base + pre] = (uint32_t)i;
     }
     base += total;
@@ -1227,13 +1247,15 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
   return hipGetLastError();
 }
 
-BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t row_f16) {
+BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t row_f16,
+                 int32_t classed) {
   BwdPlan p{};
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.n = (int32_t)nnz;
   // key bits of the largest rowref; fewest passes of at most 8 or 9 bits
   int keybits = 0;
   while (keybits < 32 && rowref_space > 1 && ((uint64_t)(rowref_space - 1) >> keybits) != 0) ++keybits;
+  if (classed) keybits += 3;  // the width class above the rowref bits
   // digit width: each tile's per-bin work (count, scan, offsets) must stay small next to its
   // per-item work, and each digit's run of a tile must stay long enough to write in whole lines.
   // Measured on MI355X with 4096-item tiles: 9-bit digits cost no more per pass than 8-bit ones,
@@ -1270,7 +1292,10 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
   const int64_t rmax = kPieceMax / ipr;
   r = r < br ? br : r > rmax ? rmax : r;
   p.rounds = (int32_t)((r + br - 1) / br * br);
+  // mixed-width tables: full pieces, each split among as many lane groups as its rows' width allows
+  if (classed) p.rounds = (int32_t)rmax;
   const int64_t pw = (int64_t)p.rounds * ipr;
+  p.pw = (int32_t)pw;
   p.n_pieces = (int32_t)((nnz + pw - 1) / pw);
   p.pdim = max_dim;
   const size_t np = (size_t)(p.n_pieces > 0 ? p.n_pieces : 1);
@@ -1321,6 +1346,12 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   s.tiles = p.tiles;
   s.tile = kBlock * p.ipt;
   s.rowref_space = a.d.rowref_space;
+  s.classed = a.d.classed;
+  s.cls_shift = a.d.cls_shift;
+  s.fgsl = a.d.fgsl;
+  s.n_fields = a.d.n_fields;
+  s.fdiv_m = a.d.fdiv_m;
+  s.fdiv_s = a.d.fdiv_s;
   s.bits = p.bits;
   const int logb = p.bits <= 8 ? 8 : p.bits;
   uint32_t* ka = reinterpret_cast<uint32_t*>(ws + p.off_ka);
@@ -1370,6 +1401,7 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   u.ctr = ctr;
   u.n_unique = a.n_unique;
   u.rounds = p.rounds;
+  u.pw = p.pw;
   u.n_pieces = p.n_pieces;
   u.pdim = p.pdim;
   u.phead = reinterpret_cast<float*>(ws + p.off_phead);
@@ -1420,6 +1452,7 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   g.unique = a.unique;
   g.count = a.count;
   g.nvalid = ctr + 2;
+  g.rmask = a.d.classed ? (1u << a.d.cls_shift) - 1u : 0xFFFFFFFFu;
   {
     KTimer tm(ctx, "seg_zero");
     EMB_LAUNCH(tm, k_zero_words, dim3(1), dim3(64), 0, ctx.stream, ctr + 2, 1);

@@ -44,7 +44,7 @@ class EmbTableInfo(C.Structure):
                 ("n_keys", C.c_uint64), ("total_elems", C.c_uint64), ("rowref_space", C.c_uint32),
                 ("granule", C.c_uint32), ("n_home", C.c_uint64 * 2), ("n_keys_t", C.c_uint64 * 2),
                 ("n_buckets", C.c_uint64 * 2), ("mean_displacement", C.c_double),
-                ("max_displacement", C.c_uint64)]
+                ("max_displacement", C.c_uint64), ("unique_by_width", C.c_uint32)]
 
 
 _LIB = None

@@ -40,8 +40,8 @@ def kernel_src_hash() -> str:
 
 
 # --------------------------------------------------------------------------- byte model
-def piece_plan(nnz, max_dim, row_f16):
-    """Lane-group size and piece length of the library's update kernels."""
+def piece_plan(nnz, max_dim, row_f16, classed=False):
+    """Piece length and count of the library's update kernels."""
     epl = 8 if row_f16 else 4
     lanes, gsl = (max_dim + epl - 1) // epl, 0
     while (1 << gsl) < lanes:
@@ -51,17 +51,26 @@ def piece_plan(nnz, max_dim, row_f16):
     r = (nnz + ipr * 131072 - 1) // (ipr * 131072)
     r = min(max(r, br), 256 // ipr)
     rounds = (r + br - 1) // br * br
+    if classed:   # mixed widths sorted by width class: full pieces
+        rounds = 256 // ipr
     return rounds * ipr, (nnz + rounds * ipr - 1) // (rounds * ipr)
 
 
-def batch_stats(w, bt, dims, rowref):
+def batch_stats(w, bt, dims, rowref, classed=False):
     """Per-batch counts the byte model needs, from the batch and the rows its keys resolve to."""
     off = bt["offsets"]
     F = w.n_fields
     bag = np.repeat(np.arange(off.size - 1, dtype=np.int64), np.diff(off.astype(np.int64)))
     width = dims[bag % F].astype(np.int64)           # row width of each occurrence
     rr = rowref.astype(np.int64)
-    if np.all(dims == dims[0]):                      # one width: no permutation needed
+    if classed:                                      # the backward sorts by (width class, rowref)
+        epl = 8 if w.row_dtype == "f16" else 4
+        cls = np.ceil(np.log2(-(-dims.astype(np.int64) // epl))).astype(np.int64)
+        key = (cls[bag % F] << 40) | rr
+        order = np.argsort(key, kind="stable")
+        srr = key[order]
+        sw = width[order]
+    elif np.all(dims == dims[0]):                    # one width: no permutation needed
         srr = np.sort(rr)
         sw = width
     else:
@@ -71,7 +80,7 @@ def batch_stats(w, bt, dims, rowref):
     heads = np.concatenate([[True], srr[1:] != srr[:-1]])
     starts = np.nonzero(heads)[0]
     ends = np.concatenate([starts[1:], [srr.size]]) - 1
-    pw, n_pieces = piece_plan(srr.size, int(dims.max()), w.row_dtype == "f16")
+    pw, n_pieces = piece_plan(srr.size, int(dims.max()), w.row_dtype == "f16", classed)
     cross = (starts // pw) != (ends // pw)          # finished by the fixup kernel
     uw = sw[starts]
     return {
@@ -189,7 +198,7 @@ def host_batch(w, T, dims, b):
     from gen import synth
     bt = synth.batch(w, b)
     rr, _ = emb.table_key_rowref(T.h, bt["keys"])
-    bt["st"] = batch_stats(w, bt, dims, rr)
+    bt["st"] = batch_stats(w, bt, dims, rr, bool(T.info["unique_by_width"]))
     return bt
 
 

@@ -89,6 +89,7 @@ typedef struct {
   uint64_t n_buckets[2];     /* 128-byte buckets per table */
   double mean_displacement;  /* mean of (slot - home) over all keys */
   uint64_t max_displacement;
+  uint32_t unique_by_width;  /* 1: sparse_adagrad_bwd lists unique rows grouped by row width */
 } EmbTableInfo;
 
 /*
@@ -162,7 +163,11 @@ int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* 
  *   d_ws       : workspace of at least bwd_workspace_bytes(n_bags, nnz) (EMB_ENOSPACE); its
  *                contents need no initialisation.
  *   d_unique   : nullable; receives the U distinct touched rowrefs in ascending order, which is
- *                ascending (table, slot) order.  Needs room for min(nnz, rows) entries.
+ *                ascending (table, slot) order.  On a mixed-width table whose info reports
+ *                unique_by_width, the list is grouped by row width first (narrowest first,
+ *                rows of 16-byte-slice counts 1, 2, 4, ... as one group each) and ascending
+ *                within each group: the backward sorts by (width, rowref) so that each update
+ *                piece sees one width.  Needs room for min(nnz, rows) entries.
  *   d_count    : nullable (only with d_unique); occurrence count of each unique rowref.
  *   d_n_unique : nullable; receives U (int64).
  * The gradient reduction and the update run in a fixed order, so results are reproducible run to

@@ -71,6 +71,13 @@ def gpu_step(T, keys, offsets, grad, out_dtype, grad_dtype, lr, eps, want_unique
     return res
 
 
+def width_class(w, dims):
+    """Per field: log2 of the 16-byte slices of its rows (rounded up to a power of two)."""
+    epl = 8 if w.row_dtype == "f16" else 4
+    lanes = -(-np.asarray(dims, dtype=np.int64) // epl)
+    return np.ceil(np.log2(lanes)).astype(np.int64)
+
+
 def run_parity(w, steps=3, batches=None, lr=None, eps=None, check_all_keys=True, flags=0):
     """Run `steps` GPU steps and the oracle side by side; check every output."""
     dims = synth.field_dims(w)
@@ -104,10 +111,17 @@ def run_parity(w, steps=3, batches=None, lr=None, eps=None, check_all_keys=True,
         # backward: unique set (ascending (table, slot)) and counts bit-exact
         u, utab, uslot, ucnt = bud.oracle_step(ot, kk, off, grad, lr, eps)
         assert res["n_unique"] == u.size
+        ucls = np.zeros(u.size, dtype=np.int64)
+        if T.info["unique_by_width"]:
+            # grouped by width class (log2 of the row's 16-byte slices), (table, slot) within
+            ucls = width_class(w, dims)[ot.field[u]]
+            order = np.argsort(ucls, kind="stable")
+            u, ucnt, ucls = u[order], ucnt[order], ucls[order]
         got_keys = emb.table_rowref_keys(T.h, res["unique"]) if u.size else np.zeros(0, np.int64)
         assert np.array_equal(got_keys.view(np.uint64), ot.keys[u])
         assert np.array_equal(res["count"], ucnt)
-        assert np.all(np.diff(res["unique"].astype(np.int64)) > 0)
+        same = np.diff(ucls) == 0
+        assert np.all(np.diff(res["unique"].astype(np.int64))[same] > 0)
         touched_keys.update(ot.keys[u].tolist())
     emb.pass_writeback(T.h)
     sel = ot.keys if check_all_keys else np.array(sorted(touched_keys), dtype=np.uint64)
