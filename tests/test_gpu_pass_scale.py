@@ -58,20 +58,24 @@ def positions(keys, want, chunk=1 << 24):
 
 
 def initial_rows(w, pos, D):
-    """Initial rows of the resident keys at positions `pos`: each field that holds one of them is
-    regenerated once (fields on a thread pool)."""
+    """Initial rows (and fp32 master copies, when the workload keeps them) of the resident keys at
+    positions `pos` of a fixed-width table: each field that holds one of them is regenerated once
+    (fields on a thread pool).  Returns (rows [n, D], master [n, D] or None)."""
     from concurrent.futures import ThreadPoolExecutor
     foff = synth.field_key_offsets(w)
-    out = np.empty((pos.size, D), dtype=np.float16)
+    out = np.empty((pos.size, D), dtype=np.float16 if w.row_dtype == "f16" else np.float32)
+    mst = np.empty((pos.size, D), dtype=np.float32) if w.has_master else None
 
     def one(f):
         sel = np.nonzero((pos >= foff[f]) & (pos < foff[f + 1]))[0]
         if sel.size:
-            r_f, _ = synth.field_state(w, f)
+            r_f, m_f = synth.field_state(w, f)
             out[sel] = r_f.reshape(-1, D)[pos[sel] - foff[f]]
+            if mst is not None:
+                mst[sel] = m_f.reshape(-1, D)[pos[sel] - foff[f]]
     with ThreadPoolExecutor(max(1, min(8, synth.worker_count()))) as ex:
         list(ex.map(one, range(w.n_fields)))
-    return out
+    return out, mst
 
 
 def test_pass_scale_sampled_parity():
@@ -132,9 +136,11 @@ def check_sampled(w, keys, bt, res, export):
     upos = np.unique(r.integers(0, keys.size, size=5000))      # untouched candidates
     upos = upos[~np.isin(keys[upos], bk)]
     t0 = time.perf_counter()
-    init = initial_rows(w, np.concatenate([wpos, upos]), D)
+    init, init_m = initial_rows(w, np.concatenate([wpos, upos]), D)
     init_want, init_u = init[:wpos.size], init[wpos.size:]
-    del init
+    m_want = None if init_m is None else init_m[:wpos.size]
+    m_u = None if init_m is None else init_m[wpos.size:]
+    del init, init_m
     say(f"initial rows of {wpos.size + upos.size} keys regenerated in "
         f"{time.perf_counter() - t0:.0f}s")
 
@@ -154,8 +160,10 @@ def check_sampled(w, keys, bt, res, export):
     say(f"{occ.size} slots, {pick.size} unique rows and counts match")
 
     # ---- pooled output of the sampled samples: the oracle over just their keys
+    fsel = np.searchsorted(want, fwd_keys)
     ot = O.Table(fwd_keys, dims, w.row_dtype, w.has_master, 1, w.load_factor, w.acc_init,
-                 init_want[np.searchsorted(want, fwd_keys)].reshape(-1))
+                 init_want[fsel].reshape(-1),
+                 master=None if m_want is None else m_want[fsel].reshape(-1))
     say(f"oracle table over {fwd_keys.size} keys of the sampled samples")
     out_o, miss_o = ot.forward(sub_keys.view(np.int64), sub_off, w.out_dtype)
     assert miss_o == 0
@@ -171,17 +179,21 @@ def check_sampled(w, keys, bt, res, export):
     upd_off = np.concatenate([[0], np.cumsum(np.bincount(bag_of[m], minlength=lens.size))])
     upd_keys = bkeys[m].view(np.int64)
     del bag_of
+    psel = np.searchsorted(want, pick_keys)
     ot = O.Table(pick_keys, dims, w.row_dtype, w.has_master, 1, w.load_factor, w.acc_init,
-                 init_want[np.searchsorted(want, pick_keys)].reshape(-1))
+                 init_want[psel].reshape(-1),
+                 master=None if m_want is None else m_want[psel].reshape(-1))
     bud = P.Budget(ot)
     t0 = time.perf_counter()
     bud.oracle_step(ot, upd_keys, upd_off, bt["grad"], w.lr, w.eps)
     say(f"oracle update of {pick.size} rows over {upd_keys.size} occurrences in "
         f"{time.perf_counter() - t0:.0f}s")
-    rows_g, acc_g, _ = export(pick_keys)
-    P.check_state(ot, bud, pick_keys, rows_g, acc_g, None)
+    rows_g, acc_g, mst_g = export(pick_keys)
+    P.check_state(ot, bud, pick_keys, rows_g, acc_g, mst_g if w.has_master else None)
     # untouched resident keys: bit-identical to their initial state
-    ru, au, _ = export(keys[upos])
+    ru, au, mu = export(keys[upos])
     assert np.all(au == np.float32(w.acc_init))
     assert ru.tobytes() == init_u.tobytes()
+    if m_u is not None:
+        assert mu.tobytes() == m_u.tobytes()
     say(f"{pick.size} updated rows within budget; {upos.size} untouched rows bit-identical")
