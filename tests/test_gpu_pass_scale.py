@@ -57,25 +57,44 @@ def positions(keys, want, chunk=1 << 24):
     return pos
 
 
-def initial_rows(w, pos, D):
+def initial_rows(w, pos):
     """Initial rows (and fp32 master copies, when the workload keeps them) of the resident keys at
-    positions `pos` of a fixed-width table: each field that holds one of them is regenerated once
-    (fields on a thread pool).  Returns (rows [n, D], master [n, D] or None)."""
+    positions `pos`, packed in that order with each key's field width; each field that holds one
+    of them is regenerated once (fields on a thread pool).
+    Returns (rows, master or None, offsets [n + 1] into both)."""
     from concurrent.futures import ThreadPoolExecutor
+    dims = synth.field_dims(w).astype(np.int64)
     foff = synth.field_key_offsets(w)
-    out = np.empty((pos.size, D), dtype=np.float16 if w.row_dtype == "f16" else np.float32)
-    mst = np.empty((pos.size, D), dtype=np.float32) if w.has_master else None
+    fld = np.searchsorted(foff, pos, side="right") - 1
+    width = dims[fld]
+    roff = np.concatenate([[0], np.cumsum(width)])
+    out = np.empty(int(roff[-1]), dtype=np.float16 if w.row_dtype == "f16" else np.float32)
+    mst = np.empty(int(roff[-1]), dtype=np.float32) if w.has_master else None
 
     def one(f):
-        sel = np.nonzero((pos >= foff[f]) & (pos < foff[f + 1]))[0]
+        sel = np.nonzero(fld == f)[0]
         if sel.size:
+            D = int(dims[f])
             r_f, m_f = synth.field_state(w, f)
-            out[sel] = r_f.reshape(-1, D)[pos[sel] - foff[f]]
+            dst = (roff[sel][:, None] + np.arange(D)[None, :]).reshape(-1)
+            src = ((pos[sel] - foff[f])[:, None] * D + np.arange(D)[None, :]).reshape(-1)
+            out[dst] = r_f[src]
             if mst is not None:
-                mst[sel] = m_f.reshape(-1, D)[pos[sel] - foff[f]]
+                mst[dst] = m_f[src]
     with ThreadPoolExecutor(max(1, min(8, synth.worker_count()))) as ex:
         list(ex.map(one, range(w.n_fields)))
-    return out, mst
+    return out, mst, roff
+
+
+def take(flat, roff, idx):
+    """The packed rows of entries `idx` (in that order) of a packed array with offsets `roff`."""
+    if flat is None:
+        return None
+    idx = np.asarray(idx, dtype=np.int64)
+    lens = roff[idx + 1] - roff[idx]
+    starts = np.repeat(roff[idx], lens)
+    within = np.arange(int(lens.sum())) - np.repeat(np.cumsum(lens) - lens, lens)
+    return flat[starts + within]
 
 
 def test_pass_scale_sampled_parity():
@@ -101,12 +120,15 @@ def test_pass_scale_sampled_parity():
     T.close()
 
 
-def check_sampled(w, keys, bt, res, export):
+def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=False):
     """The sampled checks on one step's results `res` (as gpu_step returns them) and the state
-    after it (`export(keys) -> rows, acc, master`)."""
+    after it (`export(keys) -> rows, acc, master`).  One-table fixed-width tables check rowrefs
+    against the rank the oracle derives; otherwise `rowref_keys` (the table's rowref -> key map)
+    shows that each rowref names the occurrence's key, and `unique_by_width` gives the unique
+    list's order (grouped by width class, ascending within a class)."""
     dims = synth.field_dims(w)
-    D = int(dims[0])
     F = w.n_fields
+    simple = w.n_tables == 1 and np.all(dims == dims[0])
     bkeys = bt["keys"].view(np.uint64)
     nnz = bkeys.size
     assert res["n_miss"] == 0
@@ -114,7 +136,14 @@ def check_sampled(w, keys, bt, res, export):
     bk, bcount = np.unique(bkeys, return_counts=True)
     assert res["n_unique"] == bk.size
     uq = res["unique"].astype(np.int64)
-    assert np.all(np.diff(uq) > 0)
+    if unique_by_width:
+        epl = 8 if w.row_dtype == "f16" else 4
+        wcls = np.ceil(np.log2(-(-dims.astype(np.int64) // epl))).astype(np.int64)
+        ucls = wcls[(rowref_keys(res["unique"]).view(np.uint64) >> np.uint64(48)).astype(np.int64)]
+        assert np.all(np.diff(ucls) >= 0)
+        assert np.all(np.diff(uq)[np.diff(ucls) == 0] > 0)
+    else:
+        assert np.all(np.diff(uq) > 0)
     # samples: occurrences (slots), 1 % of touched keys (counts, update), 1 sample in 64 with
     # all of its bags (pooling)
     occ = np.unique(r.integers(0, nnz, size=20_000))
@@ -136,34 +165,47 @@ def check_sampled(w, keys, bt, res, export):
     upos = np.unique(r.integers(0, keys.size, size=5000))      # untouched candidates
     upos = upos[~np.isin(keys[upos], bk)]
     t0 = time.perf_counter()
-    init, init_m = initial_rows(w, np.concatenate([wpos, upos]), D)
-    init_want, init_u = init[:wpos.size], init[wpos.size:]
-    m_want = None if init_m is None else init_m[:wpos.size]
-    m_u = None if init_m is None else init_m[wpos.size:]
-    del init, init_m
+    init, init_m, roff = initial_rows(w, np.concatenate([wpos, upos]))
+    nw = wpos.size
     say(f"initial rows of {wpos.size + upos.size} keys regenerated in "
         f"{time.perf_counter() - t0:.0f}s")
 
-    # ---- slots and rowrefs, bit-exact (one row per granule: rowref = rank in slot order)
-    nh = O.n_home_slots(keys.size, w.load_factor)
+    # ---- slots bit-exact, per table; rowrefs bit-exact (rank) or naming the right key
     t0 = time.perf_counter()
-    _, slot_o, rank_o = O.slots_of_sample(keys, nh, wpos)
+    ktab = O.table_of(keys, w.n_tables)
+    slot_o = np.empty(nw, dtype=np.int64)
+    rank_o = np.empty(nw, dtype=np.int64)
+    for t in range(w.n_tables):
+        mt = ktab == t
+        keys_t = keys[mt] if w.n_tables > 1 else keys
+        pos_in_t = (np.cumsum(mt) - 1)[wpos] if w.n_tables > 1 else wpos
+        sel = np.nonzero(ktab[wpos] == t)[0]
+        nh = O.n_home_slots(keys_t.size, w.load_factor)
+        _, sl_t, rk_t = O.slots_of_sample(keys_t, nh, pos_in_t[sel])
+        slot_o[sel] = sl_t
+        rank_o[sel] = rk_t
     say(f"oracle slots of {want.size} keys in {time.perf_counter() - t0:.0f}s")
     at = np.searchsorted(want, bkeys[occ])
     assert np.array_equal(res["slot"][occ], slot_o[at])
-    assert np.array_equal(res["rowref"][occ].astype(np.int64), rank_o[at])
-    # the unique list holds each sampled touched key's rowref, with its occurrence count
-    pr = rank_o[np.searchsorted(want, pick_keys)]
-    u_at = np.searchsorted(uq, pr)
-    assert np.array_equal(uq[u_at], pr)
+    if simple:
+        assert np.array_equal(res["rowref"][occ].astype(np.int64), rank_o[at])
+        # the unique list holds each sampled touched key's rowref, with its occurrence count
+        pr = rank_o[np.searchsorted(want, pick_keys)]
+        u_at = np.searchsorted(uq, pr)
+        assert np.array_equal(uq[u_at], pr)
+    else:
+        assert np.array_equal(rowref_keys(res["rowref"][occ]).view(np.uint64), bkeys[occ])
+        ukeys = rowref_keys(res["unique"]).view(np.uint64)
+        order = np.argsort(ukeys)
+        u_at = order[np.searchsorted(ukeys[order], pick_keys)]
+        assert np.array_equal(ukeys[u_at], pick_keys)
     assert np.array_equal(res["count"][u_at], bcount[pick])
     say(f"{occ.size} slots, {pick.size} unique rows and counts match")
 
     # ---- pooled output of the sampled samples: the oracle over just their keys
     fsel = np.searchsorted(want, fwd_keys)
-    ot = O.Table(fwd_keys, dims, w.row_dtype, w.has_master, 1, w.load_factor, w.acc_init,
-                 init_want[fsel].reshape(-1),
-                 master=None if m_want is None else m_want[fsel].reshape(-1))
+    ot = O.Table(fwd_keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor, w.acc_init,
+                 take(init, roff, fsel), master=take(init_m, roff, fsel))
     say(f"oracle table over {fwd_keys.size} keys of the sampled samples")
     out_o, miss_o = ot.forward(sub_keys.view(np.int64), sub_off, w.out_dtype)
     assert miss_o == 0
@@ -180,9 +222,8 @@ def check_sampled(w, keys, bt, res, export):
     upd_keys = bkeys[m].view(np.int64)
     del bag_of
     psel = np.searchsorted(want, pick_keys)
-    ot = O.Table(pick_keys, dims, w.row_dtype, w.has_master, 1, w.load_factor, w.acc_init,
-                 init_want[psel].reshape(-1),
-                 master=None if m_want is None else m_want[psel].reshape(-1))
+    ot = O.Table(pick_keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor,
+                 w.acc_init, take(init, roff, psel), master=take(init_m, roff, psel))
     bud = P.Budget(ot)
     t0 = time.perf_counter()
     bud.oracle_step(ot, upd_keys, upd_off, bt["grad"], w.lr, w.eps)
@@ -191,9 +232,10 @@ def check_sampled(w, keys, bt, res, export):
     rows_g, acc_g, mst_g = export(pick_keys)
     P.check_state(ot, bud, pick_keys, rows_g, acc_g, mst_g if w.has_master else None)
     # untouched resident keys: bit-identical to their initial state
+    usel = np.arange(nw, nw + upos.size)
     ru, au, mu = export(keys[upos])
     assert np.all(au == np.float32(w.acc_init))
-    assert ru.tobytes() == init_u.tobytes()
-    if m_u is not None:
-        assert mu.tobytes() == m_u.tobytes()
+    assert ru.tobytes() == take(init, roff, usel).tobytes()
+    if init_m is not None:
+        assert mu.tobytes() == take(init_m, roff, usel).tobytes()
     say(f"{pick.size} updated rows within budget; {upos.size} untouched rows bit-identical")
