@@ -199,6 +199,8 @@ struct EmbTable {
   uint64_t n_keys = 0, total_buckets = 0, total_elems = 0;
   uint32_t rowref_space = 0;
   size_t off_keys = 0, off_rows = 0, off_acc = 0, off_master = 0, off_meta = 0, arena_bytes = 0;
+  size_t off_touched = 0, touched_words = 0;  // bitmap of rowref units updated since the flash
+  std::vector<uint64_t> dirty;  // host: units written back by pass_writeback_touched since cleared
   uint8_t* image = nullptr;
   bool pinned = false;
   // pageable images move through two pinned bounce buffers (host copy of one chunk overlaps the
@@ -248,6 +250,8 @@ struct EmbTable {
     d.fgsl = meta + 3 * F;
     d.classed = classed;
     d.cls_shift = cls_shift;
+    d.touched = (flags & EMB_FLAG_TRACK_TOUCHED)
+                    ? reinterpret_cast<uint32_t*>(d_arena + off_touched) : nullptr;
     d.rowref_space = rowref_space;
     // division by the field count as a multiply and shift (exact for dividends below 2^31)
     int l = 0;
@@ -549,7 +553,9 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
   T->off_meta = align256(T->off_master + (T->has_master ? T->total_elems * 4 : 0));
   // 4 KiB of tail padding: kernels read row 0 (+ lane offset) in place of a masked-off row, which
   // must stay inside the arena even for an empty table
-  T->arena_bytes = align256(T->off_meta + 4 * 4 * (size_t)T->F) + 4096;
+  T->off_touched = align256(T->off_meta + 4 * 4 * (size_t)T->F);
+  T->touched_words = (T->flags & EMB_FLAG_TRACK_TOUCHED) ? ((size_t)T->rowref_space + 31) / 32 : 0;
+  T->arena_bytes = align256(T->off_touched + 4 * T->touched_words) + 4096;
   if (T->flags & EMB_FLAG_PINNED_STAGING) {
     hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&T->image), T->arena_bytes, 0);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the host image");
@@ -626,6 +632,8 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
       }
     }
   });
+  // the image's bitmap is all clear, so every flash starts with no row marked
+  std::memset(T->image + T->off_touched, 0, 4 * T->touched_words);
   int32_t* meta = reinterpret_cast<int32_t*>(T->image + T->off_meta);
   for (int f = 0; f < T->F; ++f) {
     meta[f] = T->dim[f];
@@ -773,6 +781,193 @@ int pass_writeback(EmbTable* t, emb_stream_t stream) {
   if (e != hipSuccess) return hip_fail(e, "pass_writeback copy");
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "pass_writeback sync");
+  return EMB_OK;
+}
+
+namespace {
+// Bytes one rowref unit takes in the compacted write-back: its index, row elements, accumulator
+// and master.
+size_t wb_unit_bytes(const EmbTable* t) {
+  const size_t g = (size_t)t->granule;
+  return 4 + g * t->elem_bytes + 4 * g + (t->has_master ? 4 * g : 0);
+}
+size_t wb_blocks(const EmbTable* t) { return (t->touched_words + kWbWords - 1) / kWbWords; }
+size_t wb_head_bytes(const EmbTable* t) { return align256(4 * (wb_blocks(t) + 1)); }
+// one half of the workspace holds at least one bitmap block's worth of units
+size_t wb_min_half(const EmbTable* t) { return align256((size_t)kWbWords * 32 * wb_unit_bytes(t) + 16); }
+
+// Compacted piece of n units: unit indices, then rows, accumulators, masters (16-byte aligned).
+struct WbPiece {
+  size_t rows, acc, master, bytes;
+};
+WbPiece wb_piece(const EmbTable* t, size_t n) {
+  const size_t g = (size_t)t->granule;
+  WbPiece p;
+  p.rows = (4 * n + 15) & ~(size_t)15;
+  p.acc = p.rows + n * g * t->elem_bytes;
+  p.master = p.acc + n * g * 4;
+  p.bytes = p.master + (t->has_master ? n * g * 4 : 0);
+  return p;
+}
+
+// Host side of one piece: each unit's row, accumulator and master into the image (runs of
+// consecutive units in one copy), and their dirty bits.
+void wb_scatter(EmbTable* t, const uint8_t* h, size_t n) {
+  const WbPiece p = wb_piece(t, n);
+  const size_t g = (size_t)t->granule, rb = g * t->elem_bytes;
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(h);
+  uint8_t* R = t->image + t->off_rows;
+  uint8_t* A = t->image + t->off_acc;
+  uint8_t* M = t->image + t->off_master;
+  parallel_for(n, [&](size_t b, size_t e) {
+    for (size_t i = b; i < e;) {
+      size_t j = i + 1;
+      while (j < e && u[j] == u[j - 1] + 1) ++j;
+      const size_t len = j - i, u0 = u[i];
+      std::memcpy(R + u0 * rb, h + p.rows + i * rb, len * rb);
+      std::memcpy(A + u0 * g * 4, h + p.acc + i * g * 4, len * g * 4);
+      if (t->has_master) std::memcpy(M + u0 * g * 4, h + p.master + i * g * 4, len * g * 4);
+      for (; i < j; ++i) __atomic_fetch_or(&t->dirty[u[i] >> 6], 1ull << (u[i] & 63), __ATOMIC_RELAXED);
+    }
+  });
+}
+}  // namespace
+
+int writeback_workspace_bytes(const EmbTable* t, size_t* min_bytes) {
+  if (!t || !min_bytes) return fail(EMB_EINVAL, "null argument");
+  if (!(t->flags & EMB_FLAG_TRACK_TOUCHED)) return fail(EMB_ESTATE, "table does not track touched rows");
+  *min_bytes = wb_head_bytes(t) + 2 * wb_min_half(t);
+  return EMB_OK;
+}
+
+int pass_writeback_touched(EmbTable* t, void* d_ws, size_t ws_bytes, int64_t* n_units_out,
+                           emb_stream_t stream) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  if (!(t->flags & EMB_FLAG_TRACK_TOUCHED)) return fail(EMB_ESTATE, "table does not track touched rows");
+  if (!t->flashed) return fail(EMB_ESTATE, "write-back before pass_flash");
+  if (!d_ws || reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(EMB_EINVAL, "workspace must be 256-byte aligned");
+  const size_t head = wb_head_bytes(t);
+  if (ws_bytes < head + 2 * wb_min_half(t)) return fail(EMB_ENOSPACE, "workspace smaller than writeback_workspace_bytes()");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t ub = wb_unit_bytes(t);
+  const bool pin = t->ensure_bounce();
+  std::vector<uint8_t> pageable[2];
+  const size_t half = ((ws_bytes - head) / 2) & ~(size_t)255;
+  const size_t host_cap = pin ? EmbTable::kBounce : half;
+  // units one piece may hold: bounded by a workspace half and a host buffer
+  const size_t cap = (std::min(half, host_cap) - 16) / ub;
+  uint8_t* ws = static_cast<uint8_t*>(d_ws);
+
+  WbLaunch a{};
+  a.touched = t->dev().touched;
+  a.n_words = (int64_t)t->touched_words;
+  a.granule = t->granule;
+  a.row_bytes = (int32_t)(t->granule * t->elem_bytes);
+  a.has_master = t->has_master;
+  a.rows = t->d_arena + t->off_rows;
+  a.acc = reinterpret_cast<const float*>(t->d_arena + t->off_acc);
+  a.master = t->has_master ? reinterpret_cast<const float*>(t->d_arena + t->off_master) : nullptr;
+  a.bcount = reinterpret_cast<uint32_t*>(ws);
+  a.blocks = (int64_t)wb_blocks(t);
+  std::vector<uint32_t> pre((size_t)a.blocks + 1, 0);
+  hipError_t e = launch_wb_count(a, st);
+  if (e == hipSuccess) e = launch_wb_scan(a, st);
+  if (e == hipSuccess && a.blocks > 0)
+    e = hipMemcpyAsync(pre.data(), a.bcount, 4 * pre.size(), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "pass_writeback_touched count");
+  if (t->dirty.empty()) t->dirty.assign(((size_t)t->rowref_space + 63) / 64, 0);
+
+  // pieces: runs of whole bitmap blocks whose units fit one piece
+  std::vector<std::pair<int64_t, int64_t>> pieces;
+  for (int64_t b0 = 0; b0 < a.blocks;) {
+    int64_t b1 = b0 + 1;
+    while (b1 < a.blocks && (size_t)(pre[(size_t)b1 + 1] - pre[(size_t)b0]) <= cap) ++b1;
+    if (pre[(size_t)b1] > pre[(size_t)b0]) pieces.emplace_back(b0, b1);
+    b0 = b1;
+  }
+  auto count = [&](size_t k) { return (size_t)(pre[(size_t)pieces[k].second] - pre[(size_t)pieces[k].first]); };
+  auto host_buf = [&](int b) -> uint8_t* {
+    if (pin) return t->bounce[b];
+    if (pageable[b].empty()) pageable[b].resize(half);
+    return pageable[b].data();
+  };
+  // piece k: compact into workspace half k % 2, copy into host buffer k % 2
+  auto issue = [&](size_t k) {
+    const int b = (int)(k & 1);
+    const size_t n = count(k);
+    const WbPiece p = wb_piece(t, n);
+    uint8_t* o = ws + head + (size_t)b * half;
+    WbLaunch g = a;
+    g.b0 = pieces[k].first;
+    g.b1 = pieces[k].second;
+    g.base = pre[(size_t)g.b0];
+    g.out_unit = reinterpret_cast<uint32_t*>(o);
+    g.out_rows = o + p.rows;
+    g.out_acc = reinterpret_cast<float*>(o + p.acc);
+    g.out_master = reinterpret_cast<float*>(o + p.master);
+    hipError_t r = launch_wb_gather(g, st);
+    if (r == hipSuccess) r = hipMemcpyAsync(host_buf(b), o, p.bytes, hipMemcpyDeviceToHost, st);
+    if (r == hipSuccess) r = pin ? hipEventRecord(t->bounce_ev[b], st) : hipStreamSynchronize(st);
+    return r;
+  };
+  if (!pieces.empty()) e = issue(0);
+  for (size_t k = 0; k < pieces.size() && e == hipSuccess; ++k) {
+    if (k + 1 < pieces.size()) e = issue(k + 1);
+    const int b = (int)(k & 1);
+    if (e == hipSuccess && pin) e = hipEventSynchronize(t->bounce_ev[b]);
+    if (e != hipSuccess) break;
+    wb_scatter(t, host_buf(b), count(k));
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "pass_writeback_touched copy");
+  if (n_units_out) *n_units_out = a.blocks > 0 ? (int64_t)pre[(size_t)a.blocks] : 0;
+  return EMB_OK;
+}
+
+int table_dirty_keys(EmbTable* t, int64_t* keys_out, int64_t cap, int64_t* n_out, int clear) {
+  if (!t || !n_out || cap < 0) return fail(EMB_EINVAL, "null argument or negative capacity");
+  int64_t n = 0;
+  if (!t->dirty.empty()) {
+    for (size_t r = 0; r < t->row_ref.size(); ++r) {
+      const uint32_t u = t->row_ref[r];
+      if (!((t->dirty[u >> 6] >> (u & 63)) & 1ull)) continue;
+      if (keys_out && n < cap) keys_out[n] = (int64_t)t->row_keys[r];
+      ++n;
+    }
+  }
+  *n_out = n;
+  if (keys_out && n > cap) return fail(EMB_ENOSPACE, "table_dirty_keys: more dirty keys than cap");
+  if (clear) std::fill(t->dirty.begin(), t->dirty.end(), 0ull);
+  return EMB_OK;
+}
+
+int table_carry_state(EmbTable* dst, const EmbTable* src, int64_t* n_carried) {
+  if (!dst || !src) return fail(EMB_EINVAL, "null table");
+  if (dst->F != src->F || dst->dim != src->dim || dst->row_dtype != src->row_dtype ||
+      dst->has_master != src->has_master)
+    return fail(EMB_EINVAL, "table_carry_state: tables differ in fields, dims, row dtype or master");
+  const size_t eb = dst->elem_bytes;
+  std::atomic<int64_t> carried{0};
+  parallel_for(dst->row_keys.size(), [&](size_t b, size_t e) {
+    int64_t c = 0;
+    for (size_t r = b; r < e; ++r) {
+      const uint64_t k = dst->row_keys[r];
+      uint32_t rr;
+      int64_t sl;
+      if (!src->probe(k, &rr, &sl)) continue;
+      const uint64_t D = (uint64_t)dst->dim[(int)(k >> 48)];
+      const uint64_t s0 = (uint64_t)rr * (uint64_t)src->granule;
+      const uint64_t d0 = (uint64_t)dst->row_ref[r] * (uint64_t)dst->granule;
+      std::memcpy(dst->image + dst->off_rows + d0 * eb, src->image + src->off_rows + s0 * eb, D * eb);
+      std::memcpy(dst->image + dst->off_acc + d0 * 4, src->image + src->off_acc + s0 * 4, D * 4);
+      if (dst->has_master)
+        std::memcpy(dst->image + dst->off_master + d0 * 4, src->image + src->off_master + s0 * 4, D * 4);
+      ++c;
+    }
+    carried += c;
+  });
+  if (n_carried) *n_carried = carried.load();
   return EMB_OK;
 }
 

@@ -62,7 +62,34 @@ struct DevDesc {
   int32_t classed;       // 1: sort keys carry the class above bit cls_shift
   int32_t cls_shift;     // bits of the rowref part of a sort key
   const int32_t* fgsl;   // [F] class (log2 lanes per row) of each field
+  uint32_t* touched;     // null, or one bit per rowref unit set when the row is updated
 };
+
+// End-of-PASS write-back of the rows touched since the last flash: the bitmap is read in blocks
+// of kWbWords words; count, scan and gather run over a range of those blocks at a time.
+constexpr int kWbWords = 1024;
+struct WbLaunch {
+  uint32_t* touched;     // the bitmap (cleared as it is gathered)
+  int64_t n_words;
+  int32_t granule;
+  int32_t row_bytes;     // bytes of one rowref unit of rows (granule * element size)
+  int32_t has_master;
+  const uint8_t* rows;
+  const float* acc;
+  const float* master;
+  uint32_t* bcount;      // [blocks + 1] set bits per block, then their exclusive prefix and total
+  int64_t blocks;
+  // gather over blocks [b0, b1): outputs at index (prefix - base)
+  int64_t b0, b1;
+  uint32_t base;
+  uint32_t* out_unit;
+  uint8_t* out_rows;
+  float* out_acc;
+  float* out_master;
+};
+hipError_t launch_wb_count(const WbLaunch& a, hipStream_t st);   // bcount = per-block counts
+hipError_t launch_wb_scan(const WbLaunch& a, hipStream_t st);    // bcount -> exclusive prefix
+hipError_t launch_wb_gather(const WbLaunch& a, hipStream_t st);  // compact blocks [b0, b1)
 
 // Kernel timing: events bracket each launch when enabled.
 struct Timing {

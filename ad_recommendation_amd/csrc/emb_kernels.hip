@@ -841,6 +841,17 @@ __device__ __forceinline__ void apply_state(const UpdArgs& a, uint32_t r, int e0
   store_from_f32<RowT, EPL>(reinterpret_cast<RowT*>(a.d.rows) + e, w);
 }
 
+// Records that the row at rowref r (D elements wide) was updated: its rowref units' bits in the
+// touched bitmap (when the table keeps one).  Called by one lane per row.  A row spans at most
+// 32 units (dims are at most 256, granules at least 8), so its bits fall in one or two words.
+__device__ __forceinline__ void mark_touched(const DevDesc& d, uint32_t r, int D) {
+  if (!d.touched) return;
+  const int units = D / d.granule;
+  const uint64_t m = ((1ull << units) - 1ull) << (r & 31u);
+  atomicOr(d.touched + (r >> 5), (uint32_t)m);
+  if ((uint32_t)(m >> 32)) atomicOr(d.touched + (r >> 5) + 1, (uint32_t)(m >> 32));
+}
+
 // Issues the load of one occurrence's upstream-gradient slice (bag `bag`, lane elements from e0);
 // returns the raw slice, the row width D of the bag's field and whether the lane is in use.
 template <typename GradT, int EPL, bool VAR>
@@ -1118,6 +1129,21 @@ __global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2)
   }
 }
 
+// Marks every row the step updated in the touched bitmap: the first occurrence of each key in
+// the sorted order, with the width of its bag's field.  Launched only for tables that keep one,
+// so the update kernels carry no extra registers for it.
+__global__ __launch_bounds__(kBlock) void k_mark_touched(UpdArgs a, uint32_t rmask) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < a.n;
+       i += (int64_t)gridDim.x * kBlock) {
+    const uint32_t k = a.key[i];
+    if (k >= a.miss_key || (i > 0 && a.key[i - 1] == k)) continue;
+    const uint32_t bag = a.val[i];
+    const uint32_t b = div_fields(a.d, bag);
+    const int f = (int)(bag - b * (uint32_t)a.d.n_fields);
+    mark_touched(a.d, k & rmask, a.d.var_dim ? a.d.fdim[f] : a.d.fixed_dim);
+  }
+}
+
 // ---------------------------------------------------------------- optional unique list output
 struct SegArgs {
   const uint32_t* key;
@@ -1207,6 +1233,81 @@ int log2_group(int dmax, int epl) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------- end-of-PASS write-back
+__global__ __launch_bounds__(kBlock) void k_wb_count(WbLaunch a) {
+  __shared__ uint32_t s_c;
+  if (threadIdx.x == 0) s_c = 0;
+  __syncthreads();
+  const int64_t w0 = (int64_t)blockIdx.x * kWbWords;
+  uint32_t c = 0;
+  for (int64_t w = w0 + threadIdx.x; w < min(a.n_words, w0 + kWbWords); w += kBlock)
+    c += __builtin_popcount(a.touched[w]);
+  if (c) atomicAdd(&s_c, c);
+  __syncthreads();
+  if (threadIdx.x == 0) a.bcount[blockIdx.x] = s_c;
+}
+
+__global__ __launch_bounds__(kBlock) void k_wb_scan(WbLaunch a) {
+  __shared__ uint32_t s_w[kWaves];
+  uint32_t carry = 0;
+  for (int64_t c0 = 0; c0 < a.blocks; c0 += kBlock) {
+    const int64_t i = c0 + threadIdx.x;
+    const uint32_t v = i < a.blocks ? a.bcount[i] : 0u;
+    uint32_t total;
+    const uint32_t pre = block_excl_scan(v, s_w, total);
+    if (i < a.blocks) a.bcount[i] = pre + carry;
+    carry += total;
+  }
+  if (threadIdx.x == 0) a.bcount[a.blocks] = carry;
+}
+
+// One block per bitmap block of the range: each thread takes 4 consecutive words, the block scan
+// of their bit counts places the set bits, and each set bit's unit (row, accumulator and master
+// elements) is copied to the compact outputs.  The words are cleared once read.
+__global__ __launch_bounds__(kBlock) void k_wb_gather(WbLaunch a) {
+  __shared__ uint32_t s_w[kWaves];
+  const int64_t blk = a.b0 + blockIdx.x;
+  const int64_t w0 = blk * kWbWords + (int64_t)threadIdx.x * 4;
+  uint32_t bits[4];
+  uint32_t c = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    bits[q] = w0 + q < a.n_words ? a.touched[w0 + q] : 0u;
+    c += __builtin_popcount(bits[q]);
+  }
+  uint32_t total;
+  uint32_t k = a.bcount[blk] - a.base + block_excl_scan(c, s_w, total);
+  const int gb = a.granule * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t m = bits[q];
+    while (m) {
+      const int b = __builtin_ctz(m);
+      m &= m - 1u;
+      const uint64_t unit = (uint64_t)(w0 + q) * 32u + (uint64_t)b;
+      a.out_unit[k] = (uint32_t)unit;
+      const uint8_t* sr = a.rows + unit * (uint64_t)a.row_bytes;
+      uint8_t* dr = a.out_rows + (uint64_t)k * a.row_bytes;
+      for (int o = 0; o < a.row_bytes; o += 16)
+        *reinterpret_cast<uint4*>(dr + o) = *reinterpret_cast<const uint4*>(sr + o);
+      const uint8_t* sa = reinterpret_cast<const uint8_t*>(a.acc + unit * (uint64_t)a.granule);
+      uint8_t* da = reinterpret_cast<uint8_t*>(a.out_acc + (uint64_t)k * a.granule);
+      for (int o = 0; o < gb; o += 16)
+        *reinterpret_cast<uint4*>(da + o) = *reinterpret_cast<const uint4*>(sa + o);
+      if (a.has_master) {
+        const uint8_t* sm = reinterpret_cast<const uint8_t*>(a.master + unit * (uint64_t)a.granule);
+        uint8_t* dm = reinterpret_cast<uint8_t*>(a.out_master + (uint64_t)k * a.granule);
+        for (int o = 0; o < gb; o += 16)
+          *reinterpret_cast<uint4*>(dm + o) = *reinterpret_cast<const uint4*>(sm + o);
+      }
+      ++k;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (w0 + q < a.n_words && bits[q]) a.touched[w0 + q] = 0u;
+}
 
 // ================================================================ launchers
 KTimer::KTimer(LaunchCtx& ctx, const char* name) : c(ctx) {
@@ -1438,6 +1539,12 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
       EMB_LAUNCH(tm, (k_update_fixup<float, false>), gpiece, blk, 0, ctx.stream, u, gsl);
     }
   }
+  if (a.d.touched) {
+    KTimer tm(ctx, "mark_touched");
+    const int64_t mb = (p.n + kBlock - 1) / kBlock;
+    EMB_LAUNCH(tm, k_mark_touched, dim3((unsigned)(mb < 4096 ? mb : 4096)), blk, 0, ctx.stream, u,
+               a.d.classed ? (1u << a.d.cls_shift) - 1u : 0xFFFFFFFFu);
+  }
   err = hipGetLastError();
   if (err != hipSuccess || !a.unique) return err;
 
@@ -1473,6 +1580,22 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
     KTimer tm(ctx, "seg_counts");
     EMB_LAUNCH(tm, k_seg_counts, dim3(1024), blk, 0, ctx.stream, g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_wb_count(const WbLaunch& a, hipStream_t st) {
+  if (a.blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_wb_count, dim3((unsigned)a.blocks), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_wb_scan(const WbLaunch& a, hipStream_t st) {
+  if (a.blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_wb_scan, dim3(1), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_wb_gather(const WbLaunch& a, hipStream_t st) {
+  if (a.b1 <= a.b0) return hipSuccess;
+  hipLaunchKernelGGL(k_wb_gather, dim3((unsigned)(a.b1 - a.b0)), dim3(kBlock), 0, st, a);
   return hipGetLastError();
 }
 

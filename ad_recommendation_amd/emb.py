@@ -18,6 +18,7 @@ ROWREF_MISS = 0xFFFFFFFF
 FLAG_PINNED_STAGING = 1
 FLAG_PROBE_COOP = 2   # force the wave-cooperative bucket probe
 FLAG_PROBE_LANE = 4   # force the one-lane-per-key bucket probe
+FLAG_TRACK_TOUCHED = 8  # keep the device bitmap of updated rows for pass_writeback_touched
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmi355emb.so")
@@ -69,6 +70,10 @@ def lib() -> C.CDLL:
         "sparse_adagrad_bwd": [_VP, _VP, _VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float, _VP,
                                C.c_size_t, _VP, _VP, _VP, _VP],
         "pass_writeback": [_VP, _VP],
+        "writeback_workspace_bytes": [_VP, C.POINTER(C.c_size_t)],
+        "pass_writeback_touched": [_VP, _VP, C.c_size_t, C.POINTER(_I64), _VP],
+        "table_dirty_keys": [_VP, _VP, _I64, C.POINTER(_I64), _I32],
+        "table_carry_state": [_VP, _VP, C.POINTER(_I64)],
         "table_export": [_VP, _VP, _I64, _VP, _VP, _VP],
         "table_fill_state": [_VP, _I64, _I64, _VP, _VP, _VP],
         "table_key_rowref": [_VP, _VP, _I64, _VP, _VP],
@@ -92,6 +97,8 @@ def exported_symbols():
     """Names include/emb.h declares (used by the load test)."""
     return ["table_create_from_prebuilt", "table_info", "table_device_bytes", "pass_flash",
             "lookup_pool_fwd", "bwd_workspace_bytes", "sparse_adagrad_bwd", "pass_writeback",
+            "writeback_workspace_bytes", "pass_writeback_touched", "table_dirty_keys",
+            "table_carry_state",
             "table_export", "table_fill_state", "table_key_rowref", "table_rowref_keys", "emb_timing_enable",
             "emb_timing_read", "table_destroy", "emb_last_error"]
 
@@ -205,6 +212,36 @@ def pass_writeback(h, stream=None):
     _check(lib().pass_writeback(h, _stream(stream)))
 
 
+def writeback_workspace_bytes(h) -> int:
+    n = C.c_size_t()
+    _check(lib().writeback_workspace_bytes(h, C.byref(n)))
+    return n.value
+
+
+def pass_writeback_touched(h, ws, stream=None) -> int:
+    """Copies back the rows updated since the flash (or the last call); returns the units moved."""
+    n = _I64()
+    _check(lib().pass_writeback_touched(h, _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                        C.byref(n), _stream(stream)))
+    return n.value
+
+
+def table_dirty_keys(h, clear: bool = False) -> np.ndarray:
+    """Keys written back by pass_writeback_touched since the last clear, in rowref order."""
+    n = _I64()
+    _check(lib().table_dirty_keys(h, None, 0, C.byref(n), 0))
+    out = np.empty(n.value, dtype=np.int64)
+    _check(lib().table_dirty_keys(h, _hp(out), int(out.size), C.byref(n), int(bool(clear))))
+    return out
+
+
+def table_carry_state(dst, src) -> int:
+    """Copies the state of the keys dst shares with src from src's host image; returns their count."""
+    n = _I64()
+    _check(lib().table_carry_state(dst, src, C.byref(n)))
+    return n.value
+
+
 def table_export(h, keys, width: int, row_dtype: int, want_master: bool):
     """Rows, accumulators (and masters) of `keys` from the host image; `width` = total elements."""
     keys = _host(np.asarray(keys).view(np.int64), np.int64)
@@ -289,6 +326,16 @@ class Table:
         if self.arena is None:
             self.arena = torch.empty(table_device_bytes(self.h), dtype=torch.uint8, device=device)
         pass_flash(self.h, self.arena, stream)
+
+    def writeback_touched(self, ws=None, stream=None) -> int:
+        import torch
+        if ws is None:
+            ws = torch.empty(writeback_workspace_bytes(self.h), dtype=torch.uint8,
+                             device=self.arena.device)
+        return pass_writeback_touched(self.h, ws, stream)
+
+    def carry_from(self, src: "Table") -> int:
+        return table_carry_state(self.h, src.h)
 
     def fill_state(self, first: int, n: int, rows=None, acc=None, master=None):
         table_fill_state(self.h, first, n, self.row_dtype, rows, acc, master)

@@ -64,6 +64,10 @@ typedef enum {
  * form's address translations thrash.  These flags force one form (both give the same results). */
 #define EMB_FLAG_PROBE_COOP 2
 #define EMB_FLAG_PROBE_LANE 4
+/* Keep a device bitmap with one bit per rowref unit, set by sparse_adagrad_bwd for every row it
+ * updates and cleared by each pass_flash, so that pass_writeback_touched can copy back only the
+ * rows a PASS changed.  Costs rowref_space / 8 bytes of arena and one atomic per updated row. */
+#define EMB_FLAG_TRACK_TOUCHED 8
 
 typedef struct {
   int32_t n_fields;          /* F, 1..65535; field id 0xFFFF is reserved for the EMPTY marker */
@@ -184,6 +188,49 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
  * same bounce buffers as pass_flash (the DMA of one chunk overlaps the host copy of the other).
  */
 int pass_writeback(EmbTable* t, emb_stream_t stream);
+
+/*
+ * Smallest workspace pass_writeback_touched accepts (host only).  A larger one moves the rows in
+ * fewer, larger pieces; a few hundred MiB reaches the copy engine's rate.  EMB_ESTATE on a table
+ * created without EMB_FLAG_TRACK_TOUCHED.
+ */
+int writeback_workspace_bytes(const EmbTable* t, size_t* min_bytes);
+
+/*
+ * End-of-PASS write-back of only the rows sparse_adagrad_bwd updated since pass_flash (or since
+ * the last pass_writeback_touched) -- the incremental form of pass_writeback, for tables created
+ * with EMB_FLAG_TRACK_TOUCHED (Tencent PCG GPU training talk: the PASS's embedding rows and
+ * optimizer state are prepared off the GPU and flashed whole; the updated ones must come back
+ * before the next PASS is built).  On the device the touched rows' units (rows, accumulators,
+ * masters, unit index) are compacted into d_ws in pieces; each piece is copied to pinned host
+ * memory and scattered into the host image while the next piece is compacted and copied.  The
+ * bitmap words it reads are cleared, so a second call moves only rows updated in between.
+ * Rows the call writes are also marked dirty for table_dirty_keys.
+ *   d_ws, ws_bytes : device workspace, 256-byte aligned, at least writeback_workspace_bytes()
+ *                    (EMB_ENOSPACE); not used by the table after the call returns.
+ *   n_units_out    : nullable; receives the number of rowref units copied (rows x their units).
+ * Synchronises `stream`.  EMB_ESTATE before pass_flash or without EMB_FLAG_TRACK_TOUCHED.
+ */
+int pass_writeback_touched(EmbTable* t, void* d_ws, size_t ws_bytes, int64_t* n_units_out,
+                           emb_stream_t stream);
+
+/*
+ * Incremental export: the keys whose rows pass_writeback_touched has written into the host image
+ * since the last call with clear != 0 (the pages' hourly incremental model beside the daily full
+ * one, Tencent PCG GPU training talk, export paragraph; table_export then reads their state).
+ * Keys come in rowref order.  keys_out may be NULL to count only; otherwise it holds cap entries
+ * and EMB_ENOSPACE is returned (nothing cleared, *n_out set) when more are dirty.  Host only.
+ */
+int table_dirty_keys(EmbTable* t, int64_t* keys_out, int64_t cap, int64_t* n_out, int clear);
+
+/*
+ * Next-PASS rebuild: for every key of `dst` also present in `src`, copy its row, accumulator and
+ * master from src's host image into dst's (the state as of src's last write-back); keys new in
+ * dst keep what they were created or filled with.  The two tables must agree on field count,
+ * field dims, row dtype and master (EMB_EINVAL otherwise).  Host only, threaded; it takes effect
+ * at dst's next pass_flash.  n_carried (nullable) receives the number of keys copied.
+ */
+int table_carry_state(EmbTable* dst, const EmbTable* src, int64_t* n_carried);
 
 /*
  * Read the host image by key: for each of the n keys, write its row (row_dtype, packed with the

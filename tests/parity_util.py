@@ -21,6 +21,17 @@ TOL_F16 = 2e-3
 F16_TINY = 2.0 ** -24
 
 
+def take(flat, roff, idx):
+    """The packed rows of entries `idx` (in that order) of a packed array with offsets `roff`."""
+    if flat is None:
+        return None
+    idx = np.asarray(idx, dtype=np.int64)
+    lens = roff[idx + 1] - roff[idx]
+    starts = np.repeat(roff[idx], lens)
+    within = np.arange(int(lens.sum())) - np.repeat(np.cumsum(lens) - lens, lens)
+    return flat[starts + within]
+
+
 def oracle_table(w, keys, rows, master, dims):
     return O.Table(keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor, w.acc_init,
                    rows, master=master)

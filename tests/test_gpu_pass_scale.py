@@ -86,17 +86,6 @@ def initial_rows(w, pos):
     return out, mst, roff
 
 
-def take(flat, roff, idx):
-    """The packed rows of entries `idx` (in that order) of a packed array with offsets `roff`."""
-    if flat is None:
-        return None
-    idx = np.asarray(idx, dtype=np.int64)
-    lens = roff[idx + 1] - roff[idx]
-    starts = np.repeat(roff[idx], lens)
-    within = np.arange(int(lens.sum())) - np.repeat(np.cumsum(lens) - lens, lens)
-    return flat[starts + within]
-
-
 def test_pass_scale_sampled_parity():
     import bench
     from tests.test_gpu_parity import gpu_step
@@ -205,7 +194,7 @@ def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=Fa
     # ---- pooled output of the sampled samples: the oracle over just their keys
     fsel = np.searchsorted(want, fwd_keys)
     ot = O.Table(fwd_keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor, w.acc_init,
-                 take(init, roff, fsel), master=take(init_m, roff, fsel))
+                 P.take(init, roff, fsel), master=P.take(init_m, roff, fsel))
     say(f"oracle table over {fwd_keys.size} keys of the sampled samples")
     out_o, miss_o = ot.forward(sub_keys.view(np.int64), sub_off, w.out_dtype)
     assert miss_o == 0
@@ -223,7 +212,7 @@ def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=Fa
     del bag_of
     psel = np.searchsorted(want, pick_keys)
     ot = O.Table(pick_keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor,
-                 w.acc_init, take(init, roff, psel), master=take(init_m, roff, psel))
+                 w.acc_init, P.take(init, roff, psel), master=P.take(init_m, roff, psel))
     bud = P.Budget(ot)
     t0 = time.perf_counter()
     bud.oracle_step(ot, upd_keys, upd_off, bt["grad"], w.lr, w.eps)
@@ -235,7 +224,7 @@ def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=Fa
     usel = np.arange(nw, nw + upos.size)
     ru, au, mu = export(keys[upos])
     assert np.all(au == np.float32(w.acc_init))
-    assert ru.tobytes() == take(init, roff, usel).tobytes()
+    assert ru.tobytes() == P.take(init, roff, usel).tobytes()
     if init_m is not None:
-        assert mu.tobytes() == take(init_m, roff, usel).tobytes()
+        assert mu.tobytes() == P.take(init_m, roff, usel).tobytes()
     say(f"{pick.size} updated rows within budget; {upos.size} untouched rows bit-identical")
