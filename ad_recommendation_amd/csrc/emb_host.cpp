@@ -7,6 +7,7 @@
 #include "emb.h"
 
 #include <hip/hip_runtime_api.h>
+#include <sys/mman.h>
 
 #include <algorithm>
 #include <atomic>
@@ -43,10 +44,20 @@ int hip_fail(hipError_t e, const char* what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Host worker threads: the hardware's count, capped at 32 and at OMP_NUM_THREADS when it is set
+// (the usual way a job states its CPU share).
 int n_threads() {
-  unsigned h = std::thread::hardware_concurrency();
-  if (h == 0) h = 4;
-  return (int)std::min(h, 32u);
+  static const int n = [] {
+    unsigned h = std::thread::hardware_concurrency();
+    if (h == 0) h = 4;
+    h = std::min(h, 32u);
+    if (const char* e = std::getenv("OMP_NUM_THREADS")) {
+      const long v = std::strtol(e, nullptr, 10);
+      if (v > 0) h = std::min(h, (unsigned)v);
+    }
+    return (int)h;
+  }();
+  return n;
 }
 
 // Run fn(begin, end) over [0, n) split across threads.
@@ -561,8 +572,13 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the host image");
     T->pinned = true;
   } else {
-    T->image = static_cast<uint8_t*>(std::aligned_alloc(4096, (T->arena_bytes + 4095) & ~(size_t)4095));
+    // 2 MiB aligned and marked for transparent huge pages: the write-back's scatter and the
+    // builder touch the image all over, and 4 KiB pages would make that TLB-bound
+    const size_t huge = 2u << 20;
+    const size_t bytes = (T->arena_bytes + huge - 1) & ~(huge - 1);
+    T->image = static_cast<uint8_t*>(std::aligned_alloc(huge, bytes));
     if (!T->image) return fail(EMB_ENOMEM, "host image allocation failed");
+    (void)madvise(T->image, bytes, MADV_HUGEPAGE);  // advice only; ignored where THP is off
   }
 
   // key buckets with per-bucket rowref prefix; per key its rowref

@@ -906,7 +906,7 @@ __device__ __forceinline__ void group_scan(int gs_log2, int g, bool& reset,
 // partial, and its last segment, when it runs into the next piece, as a tail partial;
 // k_update_fixup joins them.  The piece's sorted keys (with one neighbour on each side) and bags
 // are staged in the wave's LDS region first, with coalesced loads.
-template <typename RowT, typename GradT, bool VAR, bool MASTER>
+template <typename RowT, typename GradT, bool VAR, bool MASTER, bool TRACK>
 __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   constexpr int BR = SegBatch<EPL>::value;
@@ -950,6 +950,18 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // touched bitmap: each row is marked by the piece holding its first occurrence (a separate
+    // instantiation, so the update of untracked tables carries none of it)
+    if (TRACK) {
+      for (int j = lane; j < PW; j += 64) {
+        const uint32_t kj = sk[j + 1];
+        if (kj < a.miss_key && kj != sk[j]) {
+          const uint32_t b = div_fields(a.d, sv[j]);
+          const int f = (int)(sv[j] - b * (uint32_t)a.d.n_fields);
+          mark_touched(a.d, kj & rmask, a.d.var_dim ? a.d.fdim[f] : a.d.fixed_dim);
+        }
+      }
+    }
     // lane groups: as wide as the piece's widest rows (its last key's width class, the classes
     // being sorted above the rowrefs), else the table's widest
     int gsl = gs_log2;
@@ -1126,21 +1138,6 @@ __global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2)
       for (int q = 0; q < EPL; ++q) sum[q] += __shfl_down(sum[q], d * GS, 64);
     }
     if (lead) apply_state<RowT, EPL, MASTER>(a, k, e0, sum, st);
-  }
-}
-
-// Marks every row the step updated in the touched bitmap: the first occurrence of each key in
-// the sorted order, with the width of its bag's field.  Launched only for tables that keep one,
-// so the update kernels carry no extra registers for it.
-__global__ __launch_bounds__(kBlock) void k_mark_touched(UpdArgs a, uint32_t rmask) {
-  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < a.n;
-       i += (int64_t)gridDim.x * kBlock) {
-    const uint32_t k = a.key[i];
-    if (k >= a.miss_key || (i > 0 && a.key[i - 1] == k)) continue;
-    const uint32_t bag = a.val[i];
-    const uint32_t b = div_fields(a.d, bag);
-    const int f = (int)(bag - b * (uint32_t)a.d.n_fields);
-    mark_touched(a.d, k & rmask, a.d.var_dim ? a.d.fdim[f] : a.d.fixed_dim);
   }
 }
 
@@ -1514,7 +1511,11 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   const dim3 gpiece((unsigned)(blocks < 8192 ? blocks : 8192));
   {
     KTimer tm(ctx, "update_pieces");
-#define EMB_UPD(R, G, V, M) EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M>), gpiece, blk, 0, ctx.stream, u, gsl)
+#define EMB_UPD(R, G, V, M)                                                                   \
+  do {                                                                                        \
+    if (a.d.touched) EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M, true>), gpiece, blk, 0, ctx.stream, u, gsl); \
+    else EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M, false>), gpiece, blk, 0, ctx.stream, u, gsl);           \
+  } while (0)
     const bool var = a.d.var_dim != 0, mst = a.d.has_master != 0;
     if (a.d.row_f16) {
       if (a.grad_f16) {
@@ -1538,12 +1539,6 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
     } else {
       EMB_LAUNCH(tm, (k_update_fixup<float, false>), gpiece, blk, 0, ctx.stream, u, gsl);
     }
-  }
-  if (a.d.touched) {
-    KTimer tm(ctx, "mark_touched");
-    const int64_t mb = (p.n + kBlock - 1) / kBlock;
-    EMB_LAUNCH(tm, k_mark_touched, dim3((unsigned)(mb < 4096 ? mb : 4096)), blk, 0, ctx.stream, u,
-               a.d.classed ? (1u << a.d.cls_shift) - 1u : 0xFFFFFFFFu);
   }
   err = hipGetLastError();
   if (err != hipSuccess || !a.unique) return err;

@@ -131,6 +131,8 @@ def kernel_bytes(name, st, w, rowref_space):
         # head/tail partials of pieces whose segments cross
         return (n * 8 + st["occ_elems"] * sg + st["u_elems_inside"] * state
                 + st["u_cross"] * 2 * st["pdim"] * 4 + st["n_pieces"] * 12)
+    if name == "mark_touched":                          # sorted keys; per row its bag and bitmap word
+        return n * 4 + st["U"] * 12
     if name == "update_fixup":
         return st["n_pieces"] * 4 + st["u_cross"] * (8 + 2 * st["pdim"] * 4) + \
             st["u_elems_cross"] * state
@@ -151,7 +153,7 @@ def load_traffic(workload, kernel):
 
 
 # --------------------------------------------------------------------------- table + ring
-def build_table(w, pinned=True):
+def build_table(w, pinned=True, extra_flags=0):
     """The workload's prebuilt table with its initial state in the host image.  Tables of 64M+
     keys are created without state and filled field by field on a thread pool, so the state is
     never held twice on the host.  Returns (Table, keys, pinned)."""
@@ -169,9 +171,9 @@ def build_table(w, pinned=True):
         if not big:
             rows, master = synth.initial_state(w)
             return emb.Table(dims, rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init,
-                             keys, rows, None, master, flags=flags)
+                             keys, rows, None, master, flags=flags | extra_flags)
         return emb.Table(dims, rdt, w.has_master, w.n_tables, w.load_factor, w.acc_init, keys,
-                         flags=flags)
+                         flags=flags | extra_flags)
     T = None
     if pinned:
         try:  # pinned host image: the PASS flash is one DMA from page-locked memory
@@ -291,6 +293,9 @@ def main():
     ap.add_argument("--keys", type=int, default=0,
                     help="resident keys (0 = the workload's; other values give a scaled copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lifecycle", action="store_true",
+                    help="track touched rows (adds the marking kernel to each step) and time the "
+                         "end-of-PASS write-backs: touched rows only, then the whole state")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES, five times (counter scaling)")
     args = ap.parse_args()
@@ -319,7 +324,7 @@ def main():
     R = args.ring or w.ring
     dims = synth.field_dims(w)
     t0 = time.perf_counter()
-    T, keys, pinned = build_table(w)
+    T, keys, pinned = build_table(w, extra_flags=emb.FLAG_TRACK_TOUCHED if args.lifecycle else 0)
     log(f"[bench] {w.name}: {keys.size} keys, table built in {time.perf_counter() - t0:.1f}s; "
         f"arena {T.info['arena_bytes'] / 2**30:.2f} GiB")
     T.arena = torch.empty(emb.table_device_bytes(T.h), dtype=torch.uint8, device=dev)
@@ -406,6 +411,32 @@ def main():
     achieved = dom_bytes / (dom[1] / 1e3) / 1e9
     traffic = load_traffic(w.name, dominant)
 
+    writeback = None
+    if args.lifecycle:
+        # end of the PASS: the rows updated by every step since the flash come back to the host
+        # image, through the backward workspace (free once the steps are done)
+        wb_ws = ws if ws.numel() >= emb.writeback_workspace_bytes(T.h) else torch.empty(
+            emb.writeback_workspace_bytes(T.h), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        t_a = time.perf_counter()
+        n_units = emb.pass_writeback_touched(T.h, wb_ws)
+        t_b = time.perf_counter()
+        emb.pass_writeback(T.h)
+        t_c = time.perf_counter()
+        g = int(T.info["granule"])
+        unit_bytes = g * (2 if w.row_dtype == "f16" else 4) + 4 * g * (2 if w.has_master else 1)
+        moved = n_units * unit_bytes
+        full = int(T.info["state_bytes"])
+        writeback = {"touched_units": int(n_units), "rowref_units": int(T.info["rowref_space"]),
+                     "touched_bytes": moved, "touched_ms": (t_b - t_a) * 1e3,
+                     "touched_GB_per_s": moved / (t_b - t_a) / 1e9,
+                     "full_bytes": full, "full_ms": (t_c - t_b) * 1e3,
+                     "full_GB_per_s": full / (t_c - t_b) / 1e9,
+                     "steps_since_flash": args.warmup + R + args.steps}
+        log(f"[bench] write-back: touched {moved / 1e9:.2f} GB in {writeback['touched_ms']:.0f} ms"
+            f" ({writeback['touched_GB_per_s']:.1f} GB/s), full {full / 1e9:.2f} GB in "
+            f"{writeback['full_ms']:.0f} ms ({writeback['full_GB_per_s']:.1f} GB/s)")
+
     cpu = None
     if not args.no_cpu_baseline:
         c = run_cpu_baseline(w.name) if w.n_keys <= 50_000_000 else None
@@ -435,6 +466,7 @@ def main():
                      "alg_bytes_per_launch": dom_bytes / max(dom[0], 1)},
         "cpu_baseline": cpu,
         "pass_flash": flash,
+        "pass_writeback": writeback,
         "step_hbm": {"alg_bytes_per_step": alg_step,
                      "GB_per_s": alg_step / (ms / args.steps) / 1e6,
                      "frac": alg_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS},
