@@ -33,6 +33,13 @@ pages this project is built from):
   of features absent from the batch are left untouched (JD article, 3.2.1).
 * Mixed precision -- rows stored in fp16 with an fp32 weight copy used for the
   update, fp32 optimizer state (JD article, 3.2.3 and 5.2).
+* FTRL -- the JD article (3.2.1) names FTRL as the Adagrad variant used for
+  sparse features and says no more.  The reading taken: per-coordinate
+  FTRL-Proximal as published by McMahan et al., "Ad Click Prediction: a View
+  from the Trenches" (KDD 2013), Algorithm 1, with the squared-gradient sum n
+  being the same per-element accumulator Adagrad keeps, a per-element linear
+  state z (zero unless supplied), and the weight read from the stored row (or
+  its fp32 master copy) so that rows may start from a random initialisation.
 
 All sums are taken in float64 and rounded once to the stored type.
 """
@@ -243,7 +250,8 @@ class Table:
     def __init__(self, keys: np.ndarray, dims: Sequence[int], row_dtype: str, has_master: bool,
                  n_tables: int, load_factor: float, acc_init: float,
                  rows: np.ndarray, acc: Optional[np.ndarray] = None,
-                 master: Optional[np.ndarray] = None):
+                 master: Optional[np.ndarray] = None, ftrl: bool = False,
+                 linear: Optional[np.ndarray] = None):
         self.keys = np.ascontiguousarray(np.asarray(keys).view(np.uint64))
         self.dims = np.asarray(dims, dtype=np.int64)
         self.F = int(self.dims.size)
@@ -266,6 +274,12 @@ class Table:
                            else np.array(master, dtype=np.float32, copy=True).reshape(-1))
         else:
             self.master = None
+        # FTRL linear state z, fp32 per element
+        if ftrl:
+            self.linear = (np.zeros(total, dtype=np.float32) if linear is None
+                           else np.array(linear, dtype=np.float32, copy=True).reshape(-1))
+        else:
+            self.linear = None
         # per-table layout
         self.tab = table_of(self.keys, n_tables)
         self.n_home = []
@@ -425,6 +439,44 @@ class Table:
                 self.rows[a:b] = f16(m)
             else:
                 self.rows[a:b] = f16(self.rows[a:b].astype(np.float64) - delta)
+
+    def ftrl_rows(self, g: Dict[int, np.ndarray], alpha: float, beta: float, l1: float,
+                  l2: float) -> None:
+        """Per-coordinate FTRL-Proximal on the given rows only (McMahan et al. 2013,
+        Algorithm 1), element by element, with w the stored weight (the fp32 master
+        copy when the table keeps one, else the row):
+            n' = n + g^2
+            sigma = (sqrt(n') - sqrt(n)) / alpha
+            z' = z + g - sigma * w
+            w' = 0                                                 if |z'| <= l1
+               = -(z' - sign(z') * l1) / ((beta + sqrt(n')) / alpha + l2)   otherwise
+        n', z' and w' are computed in float64 from the stored values and rounded once
+        to their stored types (w' like the Adagrad step: fp32 row, or fp32 master and
+        fp16 row = fp16(master), or fp16 row)."""
+        assert self.linear is not None, "table keeps no FTRL linear state"
+        alpha, beta = float(np.float32(alpha)), float(np.float32(beta))
+        l1, l2 = float(np.float32(l1)), float(np.float32(l2))
+        for u, gu in g.items():
+            a, b = int(self.roff[u]), int(self.roff[u + 1])
+            n_old = self.acc[a:b].astype(np.float64)
+            n_new = n_old + gu * gu
+            w_src = self.master if self.has_master else self.rows
+            w_old = w_src[a:b].astype(np.float64)
+            sigma = (np.sqrt(n_new) - np.sqrt(n_old)) / alpha
+            z_new = self.linear[a:b].astype(np.float64) + gu - sigma * w_old
+            shrunk = z_new - np.sign(z_new) * l1
+            w_new = np.where(np.abs(z_new) <= l1, 0.0,
+                             -shrunk / ((beta + np.sqrt(n_new)) / alpha + l2))
+            self.acc[a:b] = f32(n_new)
+            self.linear[a:b] = f32(z_new)
+            if self.row_dtype == "f32":
+                self.rows[a:b] = f32(w_new)
+            elif self.has_master:
+                m = f32(w_new)
+                self.master[a:b] = m
+                self.rows[a:b] = f16(m)
+            else:
+                self.rows[a:b] = f16(w_new)
 
     def backward(self, keys: np.ndarray, offsets: np.ndarray, grad: np.ndarray,
                  lr: float, eps: float):
