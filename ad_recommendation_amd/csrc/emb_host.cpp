@@ -209,7 +209,9 @@ struct EmbTable {
   } sub[2];
   uint64_t n_keys = 0, total_buckets = 0, total_elems = 0;
   uint32_t rowref_space = 0;
-  size_t off_keys = 0, off_rows = 0, off_acc = 0, off_master = 0, off_meta = 0, arena_bytes = 0;
+  size_t off_keys = 0, off_rows = 0, off_acc = 0, off_master = 0, off_linear = 0, off_meta = 0;
+  size_t arena_bytes = 0;
+  int32_t ftrl = 0;  // the table keeps the FTRL linear state z
   size_t off_touched = 0, touched_words = 0;  // bitmap of rowref units updated since the flash
   std::vector<uint64_t> dirty;  // host: units written back by pass_writeback_touched since cleared
   uint8_t* image = nullptr;
@@ -254,6 +256,7 @@ struct EmbTable {
     d.rows = d_arena + off_rows;
     d.acc = reinterpret_cast<float*>(d_arena + off_acc);
     d.master = has_master ? reinterpret_cast<float*>(d_arena + off_master) : nullptr;
+    d.linear = ftrl ? reinterpret_cast<float*>(d_arena + off_linear) : nullptr;
     const int32_t* meta = reinterpret_cast<const int32_t*>(d_arena + off_meta);
     d.fdim = meta;
     d.fcol = meta + F;
@@ -421,6 +424,7 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
   T->F = desc->n_fields;
   T->row_dtype = desc->row_dtype;
   T->has_master = desc->has_master ? 1 : 0;
+  T->ftrl = (desc->flags & EMB_FLAG_FTRL) ? 1 : 0;
   T->n_tables = desc->n_tables;
   T->lf = desc->load_factor;
   T->acc_init = desc->acc_init;
@@ -561,7 +565,8 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
   T->off_rows = align256(T->total_buckets * 128);
   T->off_acc = align256(T->off_rows + T->total_elems * eb);
   T->off_master = align256(T->off_acc + T->total_elems * 4);
-  T->off_meta = align256(T->off_master + (T->has_master ? T->total_elems * 4 : 0));
+  T->off_linear = align256(T->off_master + (T->has_master ? T->total_elems * 4 : 0));
+  T->off_meta = align256(T->off_linear + (T->ftrl ? T->total_elems * 4 : 0));
   // 4 KiB of tail padding: kernels read row 0 (+ lane offset) in place of a masked-off row, which
   // must stay inside the arena even for an empty table
   T->off_touched = align256(T->off_meta + 4 * 4 * (size_t)T->F);
@@ -648,6 +653,11 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
       }
     }
   });
+  // FTRL linear state starts at zero
+  if (T->ftrl) {
+    uint8_t* L = T->image + T->off_linear;
+    parallel_for(T->total_elems, [&](size_t b, size_t e) { std::memset(L + 4 * b, 0, 4 * (e - b)); });
+  }
   // the image's bitmap is all clear, so every flash starts with no row marked
   std::memset(T->image + T->off_touched, 0, 4 * T->touched_words);
   int32_t* meta = reinterpret_cast<int32_t*>(T->image + T->off_meta);
@@ -743,10 +753,12 @@ int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* 
   return EMB_OK;
 }
 
-int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
-                       int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
-                       float lr, float eps, void* d_ws, size_t ws_bytes, uint32_t* d_unique,
-                       int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream) {
+namespace {
+// The backward shared by both optimizers: dedup, segmented reduction, fused element-wise update.
+int sparse_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets, int64_t n_bags,
+               int64_t nnz, const void* d_grad, int32_t grad_dtype, float lr, float eps,
+               int ftrl, float beta, float l1, float l2, void* d_ws, size_t ws_bytes,
+               uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream) {
   if (!t) return fail(EMB_EINVAL, "null table");
   if (n_bags < 0 || nnz < 0 || n_bags >= (1ll << 31) || nnz >= (1ll << 31))
     return fail(EMB_EINVAL, "n_bags and nnz must be in [0, 2^31)");
@@ -759,8 +771,12 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
   if ((reinterpret_cast<uintptr_t>(d_grad) | reinterpret_cast<uintptr_t>(d_rowref) |
        reinterpret_cast<uintptr_t>(d_ws)) % 16)
     return fail(EMB_EINVAL, "d_grad, d_rowref and d_ws must be 16-byte aligned");
+  if (ftrl && !(lr > 0.f && beta >= 0.f && l1 >= 0.f && l2 >= 0.f && std::isfinite(lr) &&
+                std::isfinite(beta) && std::isfinite(l1) && std::isfinite(l2)))
+    return fail(EMB_EINVAL, "FTRL needs alpha > 0 and finite beta, l1, l2 >= 0");
   const BwdPlan p = plan_bwd(nnz, t->rowref_space, t->max_dim, t->row_dtype == EMB_F16, t->classed);
   if (nnz > 0 && ws_bytes < p.bytes) return fail(EMB_ENOSPACE, "workspace smaller than bwd_workspace_bytes()");
+  if (ftrl && !t->ftrl) return fail(EMB_ESTATE, "table keeps no FTRL state (EMB_FLAG_FTRL)");
   if (!t->flashed) return fail(EMB_ESTATE, "backward before pass_flash");
   BwdLaunch a{};
   a.d = t->dev();
@@ -772,15 +788,37 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
   a.grad_f16 = grad_dtype == EMB_F16;
   a.lr = lr;
   a.eps = eps;
+  a.ftrl = ftrl;
+  a.beta = beta;
+  a.l1 = l1;
+  a.l2 = l2;
   a.ws = d_ws;
   a.ws_bytes = ws_bytes;
   a.unique = d_unique;
   a.count = d_count;
   a.n_unique = d_n_unique;
   LaunchCtx ctx{static_cast<hipStream_t>(stream), &t->timing};
-  hipError_t e = launch_adagrad_bwd(a, p, ctx);
-  if (e != hipSuccess) return hip_fail(e, "sparse_adagrad_bwd launch");
+  hipError_t e = launch_sparse_bwd(a, p, ctx);
+  if (e != hipSuccess) return hip_fail(e, ftrl ? "sparse_ftrl_bwd launch" : "sparse_adagrad_bwd launch");
   return EMB_OK;
+}
+}  // namespace
+
+int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                       int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
+                       float lr, float eps, void* d_ws, size_t ws_bytes, uint32_t* d_unique,
+                       int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream) {
+  return sparse_bwd(t, d_rowref, d_offsets, n_bags, nnz, d_grad, grad_dtype, lr, eps, 0, 0.f, 0.f,
+                    0.f, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
+}
+
+int sparse_ftrl_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                    int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
+                    float alpha, float beta, float l1, float l2, void* d_ws, size_t ws_bytes,
+                    uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique,
+                    emb_stream_t stream) {
+  return sparse_bwd(t, d_rowref, d_offsets, n_bags, nnz, d_grad, grad_dtype, alpha, 0.f, 1, beta,
+                    l1, l2, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
 }
 
 int pass_writeback(EmbTable* t, emb_stream_t stream) {
@@ -805,7 +843,7 @@ namespace {
 // and master.
 size_t wb_unit_bytes(const EmbTable* t) {
   const size_t g = (size_t)t->granule;
-  return 4 + g * t->elem_bytes + 4 * g + (t->has_master ? 4 * g : 0);
+  return 4 + g * t->elem_bytes + 4 * g + (t->has_master ? 4 * g : 0) + (t->ftrl ? 4 * g : 0);
 }
 size_t wb_blocks(const EmbTable* t) { return (t->touched_words + kWbWords - 1) / kWbWords; }
 size_t wb_head_bytes(const EmbTable* t) { return align256(4 * (wb_blocks(t) + 1)); }
@@ -814,7 +852,7 @@ size_t wb_min_half(const EmbTable* t) { return align256((size_t)kWbWords * 32 * 
 
 // Compacted piece of n units: unit indices, then rows, accumulators, masters (16-byte aligned).
 struct WbPiece {
-  size_t rows, acc, master, bytes;
+  size_t rows, acc, master, linear, bytes;
 };
 WbPiece wb_piece(const EmbTable* t, size_t n) {
   const size_t g = (size_t)t->granule;
@@ -822,7 +860,8 @@ WbPiece wb_piece(const EmbTable* t, size_t n) {
   p.rows = (4 * n + 15) & ~(size_t)15;
   p.acc = p.rows + n * g * t->elem_bytes;
   p.master = p.acc + n * g * 4;
-  p.bytes = p.master + (t->has_master ? n * g * 4 : 0);
+  p.linear = p.master + (t->has_master ? n * g * 4 : 0);
+  p.bytes = p.linear + (t->ftrl ? n * g * 4 : 0);
   return p;
 }
 
@@ -835,6 +874,7 @@ void wb_scatter(EmbTable* t, const uint8_t* h, size_t n) {
   uint8_t* R = t->image + t->off_rows;
   uint8_t* A = t->image + t->off_acc;
   uint8_t* M = t->image + t->off_master;
+  uint8_t* L = t->image + t->off_linear;
   parallel_for(n, [&](size_t b, size_t e) {
     for (size_t i = b; i < e;) {
       size_t j = i + 1;
@@ -843,6 +883,7 @@ void wb_scatter(EmbTable* t, const uint8_t* h, size_t n) {
       std::memcpy(R + u0 * rb, h + p.rows + i * rb, len * rb);
       std::memcpy(A + u0 * g * 4, h + p.acc + i * g * 4, len * g * 4);
       if (t->has_master) std::memcpy(M + u0 * g * 4, h + p.master + i * g * 4, len * g * 4);
+      if (t->ftrl) std::memcpy(L + u0 * g * 4, h + p.linear + i * g * 4, len * g * 4);
       for (; i < j; ++i) __atomic_fetch_or(&t->dirty[u[i] >> 6], 1ull << (u[i] & 63), __ATOMIC_RELAXED);
     }
   });
@@ -883,6 +924,7 @@ int pass_writeback_touched(EmbTable* t, void* d_ws, size_t ws_bytes, int64_t* n_
   a.rows = t->d_arena + t->off_rows;
   a.acc = reinterpret_cast<const float*>(t->d_arena + t->off_acc);
   a.master = t->has_master ? reinterpret_cast<const float*>(t->d_arena + t->off_master) : nullptr;
+  a.linear = t->ftrl ? reinterpret_cast<const float*>(t->d_arena + t->off_linear) : nullptr;
   a.bcount = reinterpret_cast<uint32_t*>(ws);
   a.blocks = (int64_t)wb_blocks(t);
   std::vector<uint32_t> pre((size_t)a.blocks + 1, 0);
@@ -922,6 +964,7 @@ int pass_writeback_touched(EmbTable* t, void* d_ws, size_t ws_bytes, int64_t* n_
     g.out_rows = o + p.rows;
     g.out_acc = reinterpret_cast<float*>(o + p.acc);
     g.out_master = reinterpret_cast<float*>(o + p.master);
+    g.out_linear = reinterpret_cast<float*>(o + p.linear);
     hipError_t r = launch_wb_gather(g, st);
     if (r == hipSuccess) r = hipMemcpyAsync(host_buf(b), o, p.bytes, hipMemcpyDeviceToHost, st);
     if (r == hipSuccess) r = pin ? hipEventRecord(t->bounce_ev[b], st) : hipStreamSynchronize(st);
@@ -961,8 +1004,8 @@ int table_dirty_keys(EmbTable* t, int64_t* keys_out, int64_t cap, int64_t* n_out
 int table_carry_state(EmbTable* dst, const EmbTable* src, int64_t* n_carried) {
   if (!dst || !src) return fail(EMB_EINVAL, "null table");
   if (dst->F != src->F || dst->dim != src->dim || dst->row_dtype != src->row_dtype ||
-      dst->has_master != src->has_master)
-    return fail(EMB_EINVAL, "table_carry_state: tables differ in fields, dims, row dtype or master");
+      dst->has_master != src->has_master || dst->ftrl != src->ftrl)
+    return fail(EMB_EINVAL, "table_carry_state: tables differ in fields, dims, row dtype, master or FTRL state");
   const size_t eb = dst->elem_bytes;
   std::atomic<int64_t> carried{0};
   parallel_for(dst->row_keys.size(), [&](size_t b, size_t e) {
@@ -979,6 +1022,8 @@ int table_carry_state(EmbTable* dst, const EmbTable* src, int64_t* n_carried) {
       std::memcpy(dst->image + dst->off_acc + d0 * 4, src->image + src->off_acc + s0 * 4, D * 4);
       if (dst->has_master)
         std::memcpy(dst->image + dst->off_master + d0 * 4, src->image + src->off_master + s0 * 4, D * 4);
+      if (dst->ftrl)
+        std::memcpy(dst->image + dst->off_linear + d0 * 4, src->image + src->off_linear + s0 * 4, D * 4);
       ++c;
     }
     carried += c;
@@ -1052,6 +1097,50 @@ int table_fill_state(EmbTable* t, int64_t first, int64_t n, const void* rows, co
       }
     }
   });
+  return EMB_OK;
+}
+
+int table_fill_linear(EmbTable* t, int64_t first, int64_t n, const float* z) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  if (!t->ftrl) return fail(EMB_EINVAL, "table keeps no FTRL state (EMB_FLAG_FTRL)");
+  if (first < 0 || n < 0 || (uint64_t)first + (uint64_t)n > t->n_keys)
+    return fail(EMB_EINVAL, "table_fill_linear: key range outside the key list given at create");
+  if (n == 0) return EMB_OK;
+  if (!z) return fail(EMB_EINVAL, "null linear state");
+  std::vector<uint64_t> off;
+  if (t->var_dim) {
+    off.resize((size_t)n + 1, 0);
+    for (int64_t i = 0; i < n; ++i) {
+      const uint64_t k = t->row_keys[t->row_of_key[(size_t)(first + i)]];
+      off[(size_t)i + 1] = off[(size_t)i] + (uint64_t)t->dim[(int)(k >> 48)];
+    }
+  }
+  float* L = reinterpret_cast<float*>(t->image + t->off_linear);
+  parallel_for((size_t)n, [&](size_t b, size_t e) {
+    for (size_t i = b; i < e; ++i) {
+      const uint32_t r = t->row_of_key[(size_t)first + i];
+      const uint64_t D = (uint64_t)t->dim[(int)(t->row_keys[r] >> 48)];
+      const uint64_t src = t->var_dim ? off[i] : (uint64_t)i * D;
+      std::memcpy(L + (uint64_t)t->row_ref[r] * (uint64_t)t->granule, z + src, D * 4);
+    }
+  });
+  return EMB_OK;
+}
+
+int table_export_linear(const EmbTable* t, const int64_t* keys, int64_t n, float* z) {
+  if (!t || (n > 0 && (!keys || !z))) return fail(EMB_EINVAL, "null argument");
+  if (!t->ftrl) return fail(EMB_EINVAL, "table keeps no FTRL state (EMB_FLAG_FTRL)");
+  const float* L = reinterpret_cast<const float*>(t->image + t->off_linear);
+  uint64_t o = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t rr;
+    int64_t sl;
+    const uint64_t k = (uint64_t)keys[i];
+    if (!t->probe(k, &rr, &sl)) return fail(EMB_EINVAL, "table_export_linear: key not in the table");
+    const uint64_t D = (uint64_t)t->dim[(int)(k >> 48)];
+    std::memcpy(z + o, L + (uint64_t)rr * (uint64_t)t->granule, D * 4);
+    o += D;
+  }
   return EMB_OK;
 }
 

@@ -51,6 +51,7 @@ struct DevDesc {
   void* rows;
   float* acc;
   float* master;
+  float* linear;         // FTRL linear state z (null unless the table keeps it)
   const int32_t* fdim;   // [F] width per field
   const int32_t* fcol;   // [F] first pooled column per field
   const int32_t* fgran;  // [F] rowref units per row of the field
@@ -77,6 +78,7 @@ struct WbLaunch {
   const uint8_t* rows;
   const float* acc;
   const float* master;
+  const float* linear;   // FTRL linear state, or null
   uint32_t* bcount;      // [blocks + 1] set bits per block, then their exclusive prefix and total
   int64_t blocks;
   // gather over blocks [b0, b1): outputs at index (prefix - base)
@@ -86,6 +88,7 @@ struct WbLaunch {
   uint8_t* out_rows;
   float* out_acc;
   float* out_master;
+  float* out_linear;
 };
 hipError_t launch_wb_count(const WbLaunch& a, hipStream_t st);   // bcount = per-block counts
 hipError_t launch_wb_scan(const WbLaunch& a, hipStream_t st);    // bcount -> exclusive prefix
@@ -139,6 +142,8 @@ struct BwdLaunch {
   const void* grad;
   int32_t grad_f16;
   float lr, eps;
+  int32_t ftrl;          // 1: FTRL-Proximal (alpha = lr), 0: Adagrad
+  float beta, l1, l2;
   void* ws;
   size_t ws_bytes;
   uint32_t* unique;
@@ -170,6 +175,6 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
 
 // Launchers (emb_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx);
-hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ctx);
+hipError_t launch_sparse_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ctx);
 
 }  // namespace emb

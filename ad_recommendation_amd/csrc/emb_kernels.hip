@@ -783,6 +783,7 @@ struct UpdArgs {
   uint32_t miss_key;
   const void* grad;
   float lr, eps;
+  float inv_alpha, beta, l1, l2;  // FTRL: 1 / alpha (alpha = lr), beta, L1 and L2 strengths
   uint32_t* ctr;         // [1] unique-row count
   int64_t* n_unique;
   // pieces: each wave reduces `rounds` x (64 / GS) consecutive sorted occurrences
@@ -796,25 +797,35 @@ struct UpdArgs {
   uint32_t* pkey;        // [n_pieces][2] row and width of the tail partial's segment
 };
 
-// Row state of one lane's EPL elements as loaded: the accumulator, and the weights the update
-// reads (the fp32 master copy when the table keeps one, else the row itself).
-template <typename RowT, int EPL, bool MASTER>
+// Row state of one lane's EPL elements as loaded: the accumulator, the weights the update reads
+// (the fp32 master copy when the table keeps one, else the row itself) and, for FTRL, the linear
+// state z.
+template <typename RowT, int EPL, bool MASTER, bool FTRL>
 struct RawState {
   typedef typename std::conditional<MASTER, float, RowT>::type WT;
   typename VecOf<float, EPL>::t acc;
   typename VecOf<WT, EPL>::t w;
 };
+template <typename RowT, int EPL, bool MASTER>
+struct RawState<RowT, EPL, MASTER, true> {
+  typedef typename std::conditional<MASTER, float, RowT>::type WT;
+  typename VecOf<float, EPL>::t acc;
+  typename VecOf<WT, EPL>::t w;
+  typename VecOf<float, EPL>::t z;
+};
 
 // Issues the state loads of row r (row 0 stands in when `on` is false).
-template <typename RowT, int EPL, bool MASTER>
-__device__ __forceinline__ RawState<RowT, EPL, MASTER> load_state(const UpdArgs& a, uint32_t r,
-                                                                  int e0, bool on) {
-  typedef typename RawState<RowT, EPL, MASTER>::WT WT;
-  RawState<RowT, EPL, MASTER> st;
+template <typename RowT, int EPL, bool MASTER, bool FTRL>
+__device__ __forceinline__ RawState<RowT, EPL, MASTER, FTRL> load_state(const UpdArgs& a,
+                                                                        uint32_t r, int e0,
+                                                                        bool on) {
+  typedef typename RawState<RowT, EPL, MASTER, FTRL>::WT WT;
+  RawState<RowT, EPL, MASTER, FTRL> st;
   const uint64_t e = (on ? (uint64_t)r * a.d.granule : 0ull) + e0;
   st.acc = load_raw<float, EPL>(a.d.acc + e);
   st.w = MASTER ? load_raw<WT, EPL>(reinterpret_cast<const WT*>(a.d.master) + e)
                 : load_raw<WT, EPL>(reinterpret_cast<const WT*>(a.d.rows) + e);
+  if constexpr (FTRL) st.z = load_raw<float, EPL>(a.d.linear + e);
   return st;
 }
 
@@ -824,13 +835,40 @@ __device__ __forceinline__ RawState<RowT, EPL, MASTER> load_state(const UpdArgs&
 // the correctly rounded forms cost ~35 instructions per element, which made them the largest
 // share of the update kernel's instructions.  The error they add to the step (a few ulp of the
 // step) is far inside the fp32 parity tolerance.
-template <typename RowT, int EPL, bool MASTER>
+//
+// FTRL-Proximal per coordinate (McMahan et al. 2013, Algorithm 1; the sparse-optimizer passage of
+// the JD article names FTRL as the Adagrad variant for sparse features), with the accumulator as
+// the squared-gradient sum n and w the stored weight:
+//   n' = n + g^2,  sigma = (sqrt(n') - sqrt(n)) / alpha,  z' = z + g - sigma * w,
+//   w' = 0 if |z'| <= l1, else -(z' - sign(z') l1) / ((beta + sqrt(n')) / alpha + l2).
+template <typename RowT, int EPL, bool MASTER, bool FTRL>
 __device__ __forceinline__ void apply_state(const UpdArgs& a, uint32_t r, int e0,
                                             typename F32V<EPL>::t g,
-                                            const RawState<RowT, EPL, MASTER>& st) {
+                                            const RawState<RowT, EPL, MASTER, FTRL>& st) {
   typedef typename F32V<EPL>::t V;
-  typedef typename RawState<RowT, EPL, MASTER>::WT WT;
+  typedef typename RawState<RowT, EPL, MASTER, FTRL>::WT WT;
   const uint64_t e = (uint64_t)r * a.d.granule + e0;
+  if constexpr (FTRL) {
+    const V n0 = to_f32<float, EPL>(st.acc);
+    const V n1 = n0 + g * g;
+    const V w0 = to_f32<WT, EPL>(st.w);
+    V z1 = to_f32<float, EPL>(st.z) + g;
+    V w1;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      const float s1 = __builtin_amdgcn_sqrtf(n1[q]);
+      const float sigma = (s1 - __builtin_amdgcn_sqrtf(n0[q])) * a.inv_alpha;
+      z1[q] -= sigma * w0[q];
+      const float den = (a.beta + s1) * a.inv_alpha + a.l2;
+      const float shrunk = z1[q] - __builtin_copysignf(a.l1, z1[q]);
+      w1[q] = __builtin_fabsf(z1[q]) <= a.l1 ? 0.0f : -shrunk * __builtin_amdgcn_rcpf(den);
+    }
+    store_from_f32<float, EPL>(a.d.acc + e, n1);
+    store_from_f32<float, EPL>(a.d.linear + e, z1);
+    if (MASTER) store_from_f32<float, EPL>(a.d.master + e, w1);
+    store_from_f32<RowT, EPL>(reinterpret_cast<RowT*>(a.d.rows) + e, w1);
+    return;
+  }
   const V acc = to_f32<float, EPL>(st.acc) + g * g;
   V den;
 #pragma unroll
@@ -906,7 +944,7 @@ __device__ __forceinline__ void group_scan(int gs_log2, int g, bool& reset,
 // partial, and its last segment, when it runs into the next piece, as a tail partial;
 // k_update_fixup joins them.  The piece's sorted keys (with one neighbour on each side) and bags
 // are staged in the wave's LDS region first, with coalesced loads.
-template <typename RowT, typename GradT, bool VAR, bool MASTER, bool TRACK>
+template <typename RowT, typename GradT, bool VAR, bool MASTER, bool TRACK, bool FTRL>
 __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   constexpr int BR = SegBatch<EPL>::value;
@@ -985,7 +1023,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
       uint32_t kk[BR];
       bool hd[BR], upd[BR], hend[BR], okg[BR];
       typename VecOf<GradT, EPL>::t gr[BR];
-      RawState<RowT, EPL, MASTER> st[BR];
+      RawState<RowT, EPL, MASTER, FTRL> st[BR];
       int D[BR];
       // issue every load of the batch: gradient slices and the state of rows ending here
 #pragma unroll
@@ -1000,7 +1038,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
         gr[r] = grad_raw<GradT, EPL, VAR>(a, sv[j], e0, own, D[r], okg[r]);
         upd[r] = end && in_grp && okg[r];
         hend[r] = end && !in_grp;
-        st[r] = load_state<RowT, EPL, MASTER>(a, kk[r] & rmask, e0, upd[r]);
+        st[r] = load_state<RowT, EPL, MASTER, FTRL>(a, kk[r] & rmask, e0, upd[r]);
       }
       if (k0 == 0) gD = D[0];
 #pragma unroll
@@ -1008,7 +1046,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
         const V x = okg[r] ? to_f32<GradT, EPL>(gr[r]) : V(0.0f);
         s = hd[r] ? x : s + x;
         heads += (hd[r] && li == 0) ? 1u : 0u;
-        if (upd[r]) apply_state<RowT, EPL, MASTER>(a, kk[r] & rmask, e0, s, st[r]);
+        if (upd[r]) apply_state<RowT, EPL, MASTER, FTRL>(a, kk[r] & rmask, e0, s, st[r]);
         if (hend[r]) {
           hsum = s;
           hends = true;
@@ -1042,9 +1080,9 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
     const bool piece_head_ends = chain_ends && cont && (g == 0 || !(rvin & 1));
     const bool row_ends = chain_ends && !piece_head_ends;
     const V total = cin + hsum;
-    const RawState<RowT, EPL, MASTER> sth =
-        load_state<RowT, EPL, MASTER>(a, kfirst & rmask, e0, row_ends && e0 < gD);
-    if (row_ends && e0 < gD) apply_state<RowT, EPL, MASTER>(a, kfirst & rmask, e0, total, sth);
+    const RawState<RowT, EPL, MASTER, FTRL> sth =
+        load_state<RowT, EPL, MASTER, FTRL>(a, kfirst & rmask, e0, row_ends && e0 < gD);
+    if (row_ends && e0 < gD) apply_state<RowT, EPL, MASTER, FTRL>(a, kfirst & rmask, e0, total, sth);
     if (piece_head_ends && e0 < gD) store_from_f32<float, EPL>(a.phead + c * a.pdim + e0, total);
     if (__ballot(piece_head_ends) != 0) flag |= kHeadEnds << 1;
     // the last group's carry runs into the next piece
@@ -1090,7 +1128,7 @@ __global__ __launch_bounds__(kBlock, 4) void k_update_pieces(UpdArgs a, int gs_l
 // it reads the flags of the following pieces 64 at a time to find where the segment ends, adds the
 // head partials of those pieces in order (lane groups take alternate pieces, then a wave
 // reduction), and applies the update to the row.
-template <typename RowT, bool MASTER>
+template <typename RowT, bool MASTER, bool FTRL>
 __global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   typedef typename F32V<EPL>::t V;
@@ -1108,7 +1146,7 @@ __global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2)
     const int D = (int)a.pkey[2 * t + 1];
     const bool on = e0 < D;
     const bool lead = g == 0 && on;
-    const RawState<RowT, EPL, MASTER> st = load_state<RowT, EPL, MASTER>(a, k, e0, lead);
+    const RawState<RowT, EPL, MASTER, FTRL> st = load_state<RowT, EPL, MASTER, FTRL>(a, k, e0, lead);
     const typename VecOf<float, EPL>::t tail =
         load_raw<float, EPL>(a.ptail + (lead ? t * a.pdim : 0) + e0);
     V sum = lead ? to_f32<float, EPL>(tail) : V(0.0f);
@@ -1137,7 +1175,7 @@ __global__ __launch_bounds__(kBlock) void k_update_fixup(UpdArgs a, int gs_log2)
 #pragma unroll
       for (int q = 0; q < EPL; ++q) sum[q] += __shfl_down(sum[q], d * GS, 64);
     }
-    if (lead) apply_state<RowT, EPL, MASTER>(a, k, e0, sum, st);
+    if (lead) apply_state<RowT, EPL, MASTER, FTRL>(a, k, e0, sum, st);
   }
 }
 
@@ -1260,8 +1298,8 @@ __global__ __launch_bounds__(kBlock) void k_wb_scan(WbLaunch a) {
 }
 
 // One block per bitmap block of the range: each thread takes 4 consecutive words, the block scan
-// of their bit counts places the set bits, and each set bit's unit (row, accumulator and master
-// elements) is copied to the compact outputs.  The words are cleared once read.
+// of their bit counts places the set bits, and each set bit's unit (row, accumulator, master and
+// FTRL linear elements) is copied to the compact outputs.  The words are cleared once read.
 __global__ __launch_bounds__(kBlock) void k_wb_gather(WbLaunch a) {
   __shared__ uint32_t s_w[kWaves];
   const int64_t blk = a.b0 + blockIdx.x;
@@ -1297,6 +1335,12 @@ __global__ __launch_bounds__(kBlock) void k_wb_gather(WbLaunch a) {
         uint8_t* dm = reinterpret_cast<uint8_t*>(a.out_master + (uint64_t)k * a.granule);
         for (int o = 0; o < gb; o += 16)
           *reinterpret_cast<uint4*>(dm + o) = *reinterpret_cast<const uint4*>(sm + o);
+      }
+      if (a.linear) {
+        const uint8_t* sz = reinterpret_cast<const uint8_t*>(a.linear + unit * (uint64_t)a.granule);
+        uint8_t* dz = reinterpret_cast<uint8_t*>(a.out_linear + (uint64_t)k * a.granule);
+        for (int o = 0; o < gb; o += 16)
+          *reinterpret_cast<uint4*>(dz + o) = *reinterpret_cast<const uint4*>(sz + o);
       }
       ++k;
     }
@@ -1420,7 +1464,22 @@ static void launch_scatter(const SortArgs& s, int ipt, int logb, dim3 grid, hipS
   else launch_scatter_ipt<FIRST, 8>(s, logb, grid, st, tm);
 }
 
-hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ctx) {
+// One launch of the update kernel for the table's row, gradient and state types; tracking and the
+// optimizer pick the instantiation.
+template <typename R, typename G, bool V, bool M>
+void launch_pieces(const UpdArgs& u, int gsl, bool track, bool ftrl, dim3 grid, hipStream_t st,
+                   KTimer& tm) {
+  const dim3 blk(kBlock);
+  if (ftrl) {
+    if (track) EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M, true, true>), grid, blk, 0, st, u, gsl);
+    else EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M, false, true>), grid, blk, 0, st, u, gsl);
+  } else {
+    if (track) EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M, true, false>), grid, blk, 0, st, u, gsl);
+    else EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M, false, false>), grid, blk, 0, st, u, gsl);
+  }
+}
+
+hipError_t launch_sparse_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ctx) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
   uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + p.off_ctr);
   if (p.n <= 0) {
@@ -1496,6 +1555,10 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   u.grad = a.grad;
   u.lr = a.lr;
   u.eps = a.eps;
+  u.inv_alpha = a.ftrl ? 1.0f / a.lr : 0.0f;
+  u.beta = a.beta;
+  u.l1 = a.l1;
+  u.l2 = a.l2;
   u.ctr = ctr;
   u.n_unique = a.n_unique;
   u.rounds = p.rounds;
@@ -1511,33 +1574,41 @@ hipError_t launch_adagrad_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& c
   const dim3 gpiece((unsigned)(blocks < 8192 ? blocks : 8192));
   {
     KTimer tm(ctx, "update_pieces");
-#define EMB_UPD(R, G, V, M)                                                                   \
-  do {                                                                                        \
-    if (a.d.touched) EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M, true>), gpiece, blk, 0, ctx.stream, u, gsl); \
-    else EMB_LAUNCH(tm, (k_update_pieces<R, G, V, M, false>), gpiece, blk, 0, ctx.stream, u, gsl);           \
-  } while (0)
     const bool var = a.d.var_dim != 0, mst = a.d.has_master != 0;
+    const bool track = a.d.touched != nullptr, ftrl = a.ftrl != 0;
     if (a.d.row_f16) {
       if (a.grad_f16) {
-        if (var) { if (mst) EMB_UPD(_Float16, _Float16, true, true); else EMB_UPD(_Float16, _Float16, true, false); }
-        else { if (mst) EMB_UPD(_Float16, _Float16, false, true); else EMB_UPD(_Float16, _Float16, false, false); }
+        if (var) { if (mst) launch_pieces<_Float16, _Float16, true, true>(u, gsl, track, ftrl, gpiece, ctx.stream, tm);
+                   else launch_pieces<_Float16, _Float16, true, false>(u, gsl, track, ftrl, gpiece, ctx.stream, tm); }
+        else { if (mst) launch_pieces<_Float16, _Float16, false, true>(u, gsl, track, ftrl, gpiece, ctx.stream, tm);
+               else launch_pieces<_Float16, _Float16, false, false>(u, gsl, track, ftrl, gpiece, ctx.stream, tm); }
       } else {
-        if (var) { if (mst) EMB_UPD(_Float16, float, true, true); else EMB_UPD(_Float16, float, true, false); }
-        else { if (mst) EMB_UPD(_Float16, float, false, true); else EMB_UPD(_Float16, float, false, false); }
+        if (var) { if (mst) launch_pieces<_Float16, float, true, true>(u, gsl, track, ftrl, gpiece, ctx.stream, tm);
+                   else launch_pieces<_Float16, float, true, false>(u, gsl, track, ftrl, gpiece, ctx.stream, tm); }
+        else { if (mst) launch_pieces<_Float16, float, false, true>(u, gsl, track, ftrl, gpiece, ctx.stream, tm);
+               else launch_pieces<_Float16, float, false, false>(u, gsl, track, ftrl, gpiece, ctx.stream, tm); }
       }
     } else {
-      if (a.grad_f16) { if (var) EMB_UPD(float, _Float16, true, false); else EMB_UPD(float, _Float16, false, false); }
-      else { if (var) EMB_UPD(float, float, true, false); else EMB_UPD(float, float, false, false); }
+      if (a.grad_f16) { if (var) launch_pieces<float, _Float16, true, false>(u, gsl, track, ftrl, gpiece, ctx.stream, tm);
+                        else launch_pieces<float, _Float16, false, false>(u, gsl, track, ftrl, gpiece, ctx.stream, tm); }
+      else { if (var) launch_pieces<float, float, true, false>(u, gsl, track, ftrl, gpiece, ctx.stream, tm);
+             else launch_pieces<float, float, false, false>(u, gsl, track, ftrl, gpiece, ctx.stream, tm); }
     }
-#undef EMB_UPD
   }
   {
     KTimer tm(ctx, "update_fixup");
+    const bool ftrl = a.ftrl != 0;
     if (a.d.row_f16) {
-      if (a.d.has_master) EMB_LAUNCH(tm, (k_update_fixup<_Float16, true>), gpiece, blk, 0, ctx.stream, u, gsl);
-      else EMB_LAUNCH(tm, (k_update_fixup<_Float16, false>), gpiece, blk, 0, ctx.stream, u, gsl);
+      if (a.d.has_master) {
+        if (ftrl) EMB_LAUNCH(tm, (k_update_fixup<_Float16, true, true>), gpiece, blk, 0, ctx.stream, u, gsl);
+        else EMB_LAUNCH(tm, (k_update_fixup<_Float16, true, false>), gpiece, blk, 0, ctx.stream, u, gsl);
+      } else {
+        if (ftrl) EMB_LAUNCH(tm, (k_update_fixup<_Float16, false, true>), gpiece, blk, 0, ctx.stream, u, gsl);
+        else EMB_LAUNCH(tm, (k_update_fixup<_Float16, false, false>), gpiece, blk, 0, ctx.stream, u, gsl);
+      }
     } else {
-      EMB_LAUNCH(tm, (k_update_fixup<float, false>), gpiece, blk, 0, ctx.stream, u, gsl);
+      if (ftrl) EMB_LAUNCH(tm, (k_update_fixup<float, false, true>), gpiece, blk, 0, ctx.stream, u, gsl);
+      else EMB_LAUNCH(tm, (k_update_fixup<float, false, false>), gpiece, blk, 0, ctx.stream, u, gsl);
     }
   }
   err = hipGetLastError();

@@ -19,6 +19,7 @@ FLAG_PINNED_STAGING = 1
 FLAG_PROBE_COOP = 2   # force the wave-cooperative bucket probe
 FLAG_PROBE_LANE = 4   # force the one-lane-per-key bucket probe
 FLAG_TRACK_TOUCHED = 8  # keep the device bitmap of updated rows for pass_writeback_touched
+FLAG_FTRL = 16          # keep the FTRL linear state for sparse_ftrl_bwd
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmi355emb.so")
@@ -69,6 +70,10 @@ def lib() -> C.CDLL:
         "bwd_workspace_bytes": [_VP, _I64, _I64, C.POINTER(C.c_size_t)],
         "sparse_adagrad_bwd": [_VP, _VP, _VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float, _VP,
                                C.c_size_t, _VP, _VP, _VP, _VP],
+        "sparse_ftrl_bwd": [_VP, _VP, _VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float, C.c_float,
+                            C.c_float, _VP, C.c_size_t, _VP, _VP, _VP, _VP],
+        "table_fill_linear": [_VP, _I64, _I64, _VP],
+        "table_export_linear": [_VP, _VP, _I64, _VP],
         "pass_writeback": [_VP, _VP],
         "writeback_workspace_bytes": [_VP, C.POINTER(C.c_size_t)],
         "pass_writeback_touched": [_VP, _VP, C.c_size_t, C.POINTER(_I64), _VP],
@@ -98,7 +103,7 @@ def exported_symbols():
     return ["table_create_from_prebuilt", "table_info", "table_device_bytes", "pass_flash",
             "lookup_pool_fwd", "bwd_workspace_bytes", "sparse_adagrad_bwd", "pass_writeback",
             "writeback_workspace_bytes", "pass_writeback_touched", "table_dirty_keys",
-            "table_carry_state",
+            "table_carry_state", "sparse_ftrl_bwd", "table_fill_linear", "table_export_linear",
             "table_export", "table_fill_state", "table_key_rowref", "table_rowref_keys", "emb_timing_enable",
             "emb_timing_read", "table_destroy", "emb_last_error"]
 
@@ -206,6 +211,30 @@ def sparse_adagrad_bwd(h, rowref, offsets, n_bags: int, nnz: int, grad, grad_dty
         _dp(grad, (torch.float32, torch.float16)), int(grad_dtype), float(lr), float(eps),
         _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(), _dp(unique, (torch.int32,)),
         _dp(count, (torch.int32,)), _dp(n_unique, (torch.int64,)), _stream(stream)))
+
+
+def sparse_ftrl_bwd(h, rowref, offsets, n_bags: int, nnz: int, grad, grad_dtype: int,
+                    alpha: float, beta: float, l1: float, l2: float, ws, unique=None, count=None,
+                    n_unique=None, stream=None):
+    import torch
+    _check(lib().sparse_ftrl_bwd(
+        h, _dp(rowref, (torch.int32,)), _dp(offsets, (torch.int32,)), int(n_bags), int(nnz),
+        _dp(grad, (torch.float32, torch.float16)), int(grad_dtype), float(alpha), float(beta),
+        float(l1), float(l2), _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _dp(unique, (torch.int32,)), _dp(count, (torch.int32,)), _dp(n_unique, (torch.int64,)),
+        _stream(stream)))
+
+
+def table_fill_linear(h, first: int, n: int, z):
+    z = _host(np.asarray(z), np.float32)
+    _check(lib().table_fill_linear(h, int(first), int(n), _hp(z)))
+
+
+def table_export_linear(h, keys, width: int) -> np.ndarray:
+    keys = _host(np.asarray(keys).view(np.int64), np.int64)
+    z = np.empty(width, dtype=np.float32)
+    _check(lib().table_export_linear(h, _hp(keys), int(keys.size), _hp(z)))
+    return z
 
 
 def pass_writeback(h, stream=None):
@@ -327,6 +356,9 @@ class Table:
             self.arena = torch.empty(table_device_bytes(self.h), dtype=torch.uint8, device=device)
         pass_flash(self.h, self.arena, stream)
 
+    def fill_linear(self, first: int, n: int, z):
+        table_fill_linear(self.h, first, n, z)
+
     def writeback_touched(self, ws=None, stream=None) -> int:
         import torch
         if ws is None:
@@ -344,6 +376,11 @@ class Table:
         k = np.asarray(keys).view(np.uint64)
         width = int(self.field_dim[(k >> np.uint64(48)).astype(np.int64)].sum())
         return table_export(self.h, k, width, self.row_dtype, self.has_master)
+
+    def export_linear(self, keys):
+        k = np.asarray(keys).view(np.uint64)
+        width = int(self.field_dim[(k >> np.uint64(48)).astype(np.int64)].sum())
+        return table_export_linear(self.h, k, width)
 
     def close(self):
         table_destroy(self.h)

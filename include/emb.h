@@ -68,6 +68,10 @@ typedef enum {
  * updates and cleared by each pass_flash, so that pass_writeback_touched can copy back only the
  * rows a PASS changed.  Costs rowref_space / 8 bytes of arena and one atomic per updated row. */
 #define EMB_FLAG_TRACK_TOUCHED 8
+/* Keep the FTRL-Proximal linear state z (fp32 per row element, zero at create) beside the
+ * accumulator, so that sparse_ftrl_bwd can update the table.  The state travels with the rows in
+ * pass_flash, both write-backs and table_carry_state. */
+#define EMB_FLAG_FTRL 16
 
 typedef struct {
   int32_t n_fields;          /* F, 1..65535; field id 0xFFFF is reserved for the EMPTY marker */
@@ -151,7 +155,8 @@ int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets
                     int64_t nnz, void* d_out, int32_t out_dtype, uint32_t* d_rowref,
                     int64_t* d_slot, int64_t* d_n_miss, emb_stream_t stream);
 
-/* Device workspace bytes sparse_adagrad_bwd needs for a batch of this shape (host only). */
+/* Device workspace bytes sparse_adagrad_bwd and sparse_ftrl_bwd need for a batch of this shape
+ * (host only). */
 int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* bytes);
 
 /*
@@ -181,6 +186,26 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
                        int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
                        float lr, float eps, void* d_ws, size_t ws_bytes, uint32_t* d_unique,
                        int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream);
+
+/*
+ * The same backward with the FTRL update in place of Adagrad, on tables created with
+ * EMB_FLAG_FTRL (EMB_ESTATE otherwise).  The JD ads article's sparse-optimizer section names FTRL
+ * as the Adagrad variant used for sparse features; the update is per-coordinate FTRL-Proximal
+ * (McMahan et al., "Ad Click Prediction: a View from the Trenches", KDD 2013, Algorithm 1), with
+ * the table's accumulator as the squared-gradient sum n, its linear state z, and w the stored
+ * weight (the fp32 master when the table keeps one, else the row).  Per touched element, with g
+ * the summed gradient:
+ *     n' = n + g*g;   sigma = (sqrt(n') - sqrt(n)) / alpha;   z' = z + g - sigma * w;
+ *     w' = 0 when |z'| <= l1, else -(z' - sign(z') * l1) / ((beta + sqrt(n')) / alpha + l2);
+ * w' is stored like the Adagrad result (fp32 row; fp32 master and fp16 row = fp16(master); fp16
+ * row).  A touched row whose z and g are zero gets weight 0.  alpha must be > 0 and beta, l1, l2
+ * finite and >= 0 (EMB_EINVAL).  Other arguments, outputs and errors as for sparse_adagrad_bwd.
+ */
+int sparse_ftrl_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                    int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
+                    float alpha, float beta, float l1, float l2, void* d_ws, size_t ws_bytes,
+                    uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique,
+                    emb_stream_t stream);
 
 /*
  * Copy rows, accumulators and masters from the device arena back into the table's host image
@@ -256,6 +281,14 @@ int table_export(const EmbTable* t, const int64_t* keys, int64_t n, void* rows, 
  */
 int table_fill_state(EmbTable* t, int64_t first, int64_t n, const void* rows, const float* acc,
                      const float* master);
+
+/*
+ * FTRL linear state in the host image (tables with EMB_FLAG_FTRL, EMB_EINVAL otherwise), packed
+ * like the create arrays: fill writes z for keys [first, first + n) of the create-time key list
+ * (it takes effect at the next pass_flash); export reads z of n keys as of the last write-back.
+ */
+int table_fill_linear(EmbTable* t, int64_t first, int64_t n, const float* z);
+int table_export_linear(const EmbTable* t, const int64_t* keys, int64_t n, float* z);
 
 /* Host-side lookup of n keys: rowref (EMB_ROWREF_MISS if absent) and logical slot (-1). */
 int table_key_rowref(const EmbTable* t, const int64_t* keys, int64_t n, uint32_t* rowref,

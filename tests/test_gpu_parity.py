@@ -39,7 +39,9 @@ def gpu_table(w, keys, rows, master, dims, flags=0):
     return T
 
 
-def gpu_step(T, keys, offsets, grad, out_dtype, grad_dtype, lr, eps, want_unique=True):
+def gpu_step(T, keys, offsets, grad, out_dtype, grad_dtype, lr, eps, want_unique=True, ftrl=None):
+    """One forward + backward through the C ABI; `ftrl` = (alpha, beta, l1, l2) runs the FTRL
+    update instead of Adagrad (lr and eps are then unused)."""
     dev = "cuda"
     F = T.n_fields
     k = torch.from_numpy(np.ascontiguousarray(keys)).to(dev)
@@ -55,7 +57,10 @@ def gpu_step(T, keys, offsets, grad, out_dtype, grad_dtype, lr, eps, want_unique
     uniq = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev) if want_unique else None
     cnt = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev) if want_unique else None
     nu = torch.full((1,), -1, dtype=torch.int64, device=dev)
-    emb.sparse_adagrad_bwd(T.h, rowref, o, n_bags, nnz, g, DT[grad_dtype], lr, eps, ws, uniq, cnt, nu)
+    if ftrl is None:
+        emb.sparse_adagrad_bwd(T.h, rowref, o, n_bags, nnz, g, DT[grad_dtype], lr, eps, ws, uniq, cnt, nu)
+    else:
+        emb.sparse_ftrl_bwd(T.h, rowref, o, n_bags, nnz, g, DT[grad_dtype], *ftrl, ws, uniq, cnt, nu)
     torch.cuda.synchronize()
     U = int(nu.item())
     res = {
