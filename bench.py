@@ -26,6 +26,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "embedding rows looked up+updated/sec (fwd+bwd) and achieved HBM GB/s vs peak"
+# FTRL-Proximal hyperparameters besides alpha (the workload's learning rate)
+FTRL_BETA, FTRL_L1, FTRL_L2 = 1.0, 0.01, 0.1
 KERNEL_SRC = os.path.join(ROOT, "ad_recommendation_amd", "csrc", "emb_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -104,14 +106,14 @@ def sort_plan(nnz, rowref_space):
     return ipt, (nnz + 256 * ipt - 1) // (256 * ipt), bits
 
 
-def kernel_bytes(name, st, w, rowref_space):
+def kernel_bytes(name, st, w, rowref_space, ftrl=False):
     """Algorithmic bytes one launch of `name` moves for a batch with stats `st`: every datum the
     kernel must read or write once (no cache reuse), as in the design's byte model."""
     sr = 2 if w.row_dtype == "f16" else 4
     so = 2 if w.out_dtype == "f16" else 4
     sg = 2 if w.grad_dtype == "f16" else 4
     m = 1 if w.has_master else 0
-    state = 2 * sr + 8 + 8 * m                          # per element: row r/w, acc r/w, master r/w
+    state = 2 * sr + 8 + 8 * m + (8 if ftrl else 0)    # per element: row, acc, master, z r/w
     n = st["nnz"]
     if name == "lookup_pool":
         # key in, slot hit (key compare + row prefix), row gather, rowref out; offsets, pooled out
@@ -231,7 +233,7 @@ def stage_ring(w, T, dims, R, dev):
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline_child(name: str, min_seconds: float, max_batches: int):
+def cpu_baseline_child(name: str, min_seconds: float, max_batches: int, optimizer: str = "adagrad"):
     """Time the oracle's forward + backward (one thread) on consecutive batches of the workload,
     from batch 0, until at least min_seconds of oracle work or max_batches batches are done."""
     from gen import synth, workloads as W
@@ -241,8 +243,9 @@ def cpu_baseline_child(name: str, min_seconds: float, max_batches: int):
     rows, master = synth.initial_state(w)
     dims = synth.field_dims(w)
     t0 = time.perf_counter()
+    ftrl = optimizer == "ftrl"
     ot = O.Table(keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor, w.acc_init, rows,
-                 master=master)
+                 master=master, ftrl=ftrl)
     build_s = time.perf_counter() - t0
     t = t_fwd = 0.0
     nnz = n_u = nb = 0
@@ -251,7 +254,12 @@ def cpu_baseline_child(name: str, min_seconds: float, max_batches: int):
         t0 = time.perf_counter()
         ot.forward(bt["keys"], bt["offsets"], w.out_dtype)
         t1 = time.perf_counter()
-        u, _, _, _ = ot.backward(bt["keys"], bt["offsets"], bt["grad"], w.lr, w.eps)
+        if ftrl:
+            u, _, _, _ = ot.touched(bt["keys"], bt["offsets"])
+            ot.ftrl_rows(ot.row_grads(bt["keys"], bt["offsets"], bt["grad"]), w.lr, FTRL_BETA,
+                         FTRL_L1, FTRL_L2)
+        else:
+            u, _, _, _ = ot.backward(bt["keys"], bt["offsets"], bt["grad"], w.lr, w.eps)
         t += time.perf_counter() - t0
         t_fwd += t1 - t0
         nnz += int(bt["keys"].size)
@@ -270,10 +278,11 @@ def cpu_baseline_child(name: str, min_seconds: float, max_batches: int):
                       "nproc": os.cpu_count()}))
 
 
-def run_cpu_baseline(name: str):
+def run_cpu_baseline(name: str, optimizer: str = "adagrad"):
     env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
     code = ("import os,sys; os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]}); "
-            f"sys.path.insert(0, {ROOT!r}); import bench; bench.cpu_baseline_child({name!r}, 12.0, 64)")
+            f"sys.path.insert(0, {ROOT!r}); import bench; "
+            f"bench.cpu_baseline_child({name!r}, 12.0, 64, {optimizer!r})")
     r = subprocess.run([sys.executable, "-c", code], env=env, stdout=subprocess.PIPE,
                        stderr=subprocess.PIPE, text=True, timeout=900)
     if r.returncode != 0:
@@ -293,6 +302,9 @@ def main():
     ap.add_argument("--keys", type=int, default=0,
                     help="resident keys (0 = the workload's; other values give a scaled copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--optimizer", choices=("adagrad", "ftrl"), default="adagrad",
+                    help="sparse update: Adagrad, or FTRL-Proximal (alpha = the workload's lr, "
+                         f"beta {FTRL_BETA}, l1 {FTRL_L1}, l2 {FTRL_L2})")
     ap.add_argument("--lifecycle", action="store_true",
                     help="track touched rows (adds the marking kernel to each step) and time the "
                          "end-of-PASS write-backs: touched rows only, then the whole state")
@@ -324,7 +336,9 @@ def main():
     R = args.ring or w.ring
     dims = synth.field_dims(w)
     t0 = time.perf_counter()
-    T, keys, pinned = build_table(w, extra_flags=emb.FLAG_TRACK_TOUCHED if args.lifecycle else 0)
+    ftrl = args.optimizer == "ftrl"
+    T, keys, pinned = build_table(w, extra_flags=(emb.FLAG_TRACK_TOUCHED if args.lifecycle else 0) |
+                                  (emb.FLAG_FTRL if ftrl else 0))
     log(f"[bench] {w.name}: {keys.size} keys, table built in {time.perf_counter() - t0:.1f}s; "
         f"arena {T.info['arena_bytes'] / 2**30:.2f} GiB")
     T.arena = torch.empty(emb.table_device_bytes(T.h), dtype=torch.uint8, device=dev)
@@ -360,8 +374,13 @@ def main():
         r = ring[i % R]
         emb.lookup_pool_fwd(T.h, r["keys"], r["offsets"], r["n_bags"], r["nnz"], out,
                             out_code, rowref)
-        emb.sparse_adagrad_bwd(T.h, rowref, r["offsets"], r["n_bags"], r["nnz"], r["grad"],
-                               g_code, w.lr, w.eps, ws, n_unique=n_unique[i % R:i % R + 1])
+        if ftrl:
+            emb.sparse_ftrl_bwd(T.h, rowref, r["offsets"], r["n_bags"], r["nnz"], r["grad"],
+                                g_code, w.lr, FTRL_BETA, FTRL_L1, FTRL_L2, ws,
+                                n_unique=n_unique[i % R:i % R + 1])
+        else:
+            emb.sparse_adagrad_bwd(T.h, rowref, r["offsets"], r["n_bags"], r["nnz"], r["grad"],
+                                   g_code, w.lr, w.eps, ws, n_unique=n_unique[i % R:i % R + 1])
 
     for i in range(args.warmup):
         step(i)
@@ -377,7 +396,7 @@ def main():
     dominant = max(calib, key=lambda k: calib[k][1] / max(calib[k][0], 1))
     kernels = {}
     for k, (cnt, kms) in calib.items():
-        b = np.mean([kernel_bytes(k, r["st"], w, rowref_space) for r in ring]) * cnt / R
+        b = np.mean([kernel_bytes(k, r["st"], w, rowref_space, ftrl) for r in ring]) * cnt / R
         kernels[k] = {"launches_per_step": cnt / R, "ms_per_step": kms / R,
                       "alg_bytes_per_step": float(b), "GB_per_s": float(b / (kms / R) / 1e6)}
     alg_step = sum(v["alg_bytes_per_step"] for v in kernels.values())
@@ -406,7 +425,8 @@ def main():
     value = rows_done / (ms / 1e3)
     # algorithmic bytes of the dominant kernel over its timed launches
     per_step_launches = dom[0] / args.steps
-    dom_bytes = sum(kernel_bytes(dominant, ring[i % R]["st"], w, rowref_space) for i in range(args.steps))
+    dom_bytes = sum(kernel_bytes(dominant, ring[i % R]["st"], w, rowref_space, ftrl)
+                    for i in range(args.steps))
     dom_bytes *= per_step_launches
     achieved = dom_bytes / (dom[1] / 1e3) / 1e9
     traffic = load_traffic(w.name, dominant)
@@ -424,7 +444,8 @@ def main():
         emb.pass_writeback(T.h)
         t_c = time.perf_counter()
         g = int(T.info["granule"])
-        unit_bytes = g * (2 if w.row_dtype == "f16" else 4) + 4 * g * (2 if w.has_master else 1)
+        unit_bytes = g * (2 if w.row_dtype == "f16" else 4) + 4 * g * (
+            1 + (1 if w.has_master else 0) + (1 if ftrl else 0))
         moved = n_units * unit_bytes
         full = int(T.info["state_bytes"])
         writeback = {"touched_units": int(n_units), "rowref_units": int(T.info["rowref_space"]),
@@ -439,7 +460,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        c = run_cpu_baseline(w.name) if w.n_keys <= 50_000_000 else None
+        c = run_cpu_baseline(w.name, args.optimizer) if w.n_keys <= 50_000_000 else None
         if c:
             cpu = {"value": (c["nnz"] + c["U"]) / c["seconds"], "unit": "rows/s", "cores": 1,
                    "kind": "oracle",
@@ -456,6 +477,7 @@ def main():
         "config": {"workload": w.name, "fields": w.n_fields, "resident_keys": w.n_keys,
                    "dim": w.dim if w.dim else "per-field", "row_dtype": w.row_dtype,
                    "master": w.has_master, "tables": w.n_tables, "batch": w.batch,
+                   "optimizer": args.optimizer,
                    "ring": R, "mean_lookups_per_step": float(np.mean([r["nnz"] for r in ring])),
                    "mean_rows_updated_per_step": float(np.mean([r["st"]["U"] for r in ring])),
                    "parallelism": "single GPU"},
