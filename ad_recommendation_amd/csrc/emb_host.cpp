@@ -400,9 +400,188 @@ extern "C" {
 
 const char* emb_last_error(void) { return g_err.c_str(); }
 
+namespace {
+// Device resources for building the layout on the GPU (table_create_on_device).
+struct DevBuild {
+  uint8_t* ws;
+  size_t ws_bytes;
+  hipStream_t st;
+};
+
+// Workspace carve-up of the device build for n keys.  The sort region holds the radix sort's
+// buffers for any sort-key space: the widest plan plus room for 9-bit digits on every tile.
+struct BuildPlan {
+  size_t off_keys, off_sort, sort_bytes, off_gran, off_bmax, off_bsum, off_misc, off_buckets, bytes;
+  int64_t max_blocks;
+  uint64_t max_buckets;
+};
+BuildPlan plan_build(int64_t n, uint64_t bucket_bound, int F) {
+  BuildPlan b{};
+  const BwdPlan wide = plan_bwd(n, 0xFFFFFFFFu, 8, 0, 0);
+  b.sort_bytes = wide.bytes + 4 * 513 * ((size_t)wide.tiles + (size_t)wide.groups + 2) + 4096;
+  size_t o = 0;
+  b.off_keys = o; o = align256(o + 8 * (size_t)n);
+  b.off_sort = o; o = align256(o + b.sort_bytes);
+  b.off_gran = o; o = align256(o + 4 * (size_t)F);
+  b.max_blocks = (n + (int64_t)kBuildTile - 1) / ((int64_t)kBuildTile) + 1;
+  b.off_bmax = o; o = align256(o + 8 * (size_t)(b.max_blocks + 1));
+  b.off_bsum = o; o = align256(o + 4 * (size_t)(b.max_blocks + 1));
+  b.off_misc = o; o = align256(o + 64);
+  b.max_buckets = bucket_bound;
+  b.off_buckets = o; o = align256(o + 128 * (size_t)bucket_bound);
+  b.bytes = o;
+  return b;
+}
+// Buckets a table of n keys can need at most: its home slots plus one slot per key of overflow,
+// plus the terminator; for two tables, both.
+uint64_t bucket_bound(int64_t n, double lf, int n_tables) {
+  const uint64_t nh = (uint64_t)std::ceil((double)n / lf) + 2 * (uint64_t)n_tables;
+  return (nh + (uint64_t)n + (uint64_t)kKeysPerBucket * n_tables) / kKeysPerBucket + 2 * (uint64_t)n_tables;
+}
+
+// The ordered linear-probing layout computed on the GPU: same slots, rowrefs and buckets as the
+// host builder.  On return `order` holds the caller index of each key in rowref order and the
+// bucket words sit in the workspace at d_buckets.
+int device_layout(EmbTable* T, const uint64_t* K, size_t N, const DevBuild& db,
+                  std::vector<uint32_t>& order, uint64_t*& d_buckets, double& disp_sum) {
+  const uint64_t nh0 = T->sub[0].n_home, nh1 = T->n_tables == 2 ? T->sub[1].n_home : 0;
+  if (nh0 + nh1 >= 0xFFFFFFF0ull) return fail(EMB_ERANGE, "too many home slots for the device build");
+  const BuildPlan bp = plan_build((int64_t)N, bucket_bound((int64_t)N, T->lf, T->n_tables), T->F);
+  if (db.ws_bytes < bp.bytes) return fail(EMB_ENOSPACE, "workspace smaller than table_build_workspace_bytes()");
+  uint8_t* ws = db.ws;
+  hipStream_t st = db.st;
+  BuildArgs a{};
+  a.keys = reinterpret_cast<const uint64_t*>(ws + bp.off_keys);
+  a.n = (int64_t)N;
+  a.n_tables = T->n_tables;
+  a.n_home0 = (uint32_t)nh0;
+  a.n_home1 = (uint32_t)nh1;
+  a.gran = reinterpret_cast<const int32_t*>(ws + bp.off_gran);
+  uint8_t* sws = ws + bp.off_sort;
+  const BwdPlan sp = plan_bwd((int64_t)N, (uint32_t)(nh0 + nh1), 8, 0, 0);
+  if (sp.bytes > bp.sort_bytes) return fail(EMB_ENOSPACE, "device build: sort plan exceeds its region");
+  a.skey = reinterpret_cast<uint32_t*>(sws + sp.off_ka);
+  a.sval = reinterpret_cast<uint32_t*>(sws + sp.off_va);
+  uint32_t* misc = reinterpret_cast<uint32_t*>(ws + bp.off_misc);
+  a.dup = misc;
+  a.disp = reinterpret_cast<unsigned long long*>(misc + 2);
+  a.bmax = reinterpret_cast<int64_t*>(ws + bp.off_bmax);
+  a.bsum = reinterpret_cast<uint32_t*>(ws + bp.off_bsum);
+  a.buckets = reinterpret_cast<uint64_t*>(ws + bp.off_buckets);
+  hipError_t e = hipMemsetAsync(misc, 0, 64, st);
+  if (e == hipSuccess && N) e = hipMemcpyAsync(ws + bp.off_keys, K, 8 * N, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(ws + bp.off_gran, T->gran.data(), 4 * (size_t)T->F, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = launch_build_homes(a, st);
+  uint32_t *ks = a.skey, *vs = a.sval;
+  if (e == hipSuccess) e = launch_build_sort(a, sp, sws, &ks, &vs, st);
+  a.sk = ks;
+  a.sv = vs;
+  if (e == hipSuccess) e = launch_build_ties(a, st);
+  uint32_t dup = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&dup, a.dup, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "device layout build (sort)");
+  if (dup) return fail(EMB_EDUPKEY, "duplicate key in the prebuilt key set");
+
+  // per table: slot and unit scans, then the table's bucket count and bases
+  const size_t n0 = T->sub[0].n_keys;
+  int64_t seg[2][2] = {{0, (int64_t)n0}, {(int64_t)n0, (int64_t)N}};
+  uint64_t rr = 0, bb = 0;
+  int64_t lastm[2] = {0, 0};
+  for (int t = 0; t < T->n_tables; ++t) {
+    EmbTable::Sub& s = T->sub[t];
+    BuildArgs g = a;
+    g.s0 = seg[t][0];
+    g.s1 = seg[t][1];
+    g.home_base = t ? (uint32_t)nh0 : 0u;
+    g.blocks = (g.s1 - g.s0 + (int64_t)kBuildTile - 1) / ((int64_t)kBuildTile);
+    int64_t tot_m = 0;
+    uint32_t tot_u = 0;
+    if (g.blocks > 0) {
+      e = launch_build_scan(g, st);
+      if (e == hipSuccess) e = hipMemcpyAsync(&tot_m, g.bmax + g.blocks, 8, hipMemcpyDeviceToHost, st);
+      if (e == hipSuccess) e = hipMemcpyAsync(&tot_u, g.bsum + g.blocks, 4, hipMemcpyDeviceToHost, st);
+      if (e == hipSuccess) e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return hip_fail(e, "device layout build (scan)");
+    }
+    lastm[t] = tot_m;
+    const uint64_t nt = (uint64_t)(g.s1 - g.s0);
+    const uint64_t last = nt ? (nt - 1) + (uint64_t)tot_m : 0;
+    const uint64_t span = std::max<uint64_t>(s.n_home, nt ? last + 1 : 0);
+    s.n_buckets = (span + kKeysPerBucket - 1) / kKeysPerBucket + 1;
+    if (s.n_buckets > 0xFFFFFFF0ull) return fail(EMB_ERANGE, "table too large");
+    s.bucket_base = bb;
+    bb += s.n_buckets;
+    s.rowref_base = (uint32_t)rr;
+    rr += tot_u;
+    if (rr >= 0xFFFFFFFFull) return fail(EMB_ERANGE, "rowref space exceeds 32 bits");
+  }
+  if (bb > bp.max_buckets) return fail(EMB_ERANGE, "device build: bucket bound exceeded");
+  T->total_buckets = bb;
+  T->rowref_space = (uint32_t)rr;
+  // every key word starts EMPTY; then keys, prefix words and the tail of each table
+  e = hipMemsetAsync(a.buckets, 0xFF, 128 * (size_t)bb, st);
+  for (int t = 0; t < T->n_tables && e == hipSuccess; ++t) {
+    EmbTable::Sub& s = T->sub[t];
+    BuildArgs g = a;
+    g.s0 = seg[t][0];
+    g.s1 = seg[t][1];
+    g.home_base = t ? (uint32_t)nh0 : 0u;
+    g.blocks = (g.s1 - g.s0 + (int64_t)kBuildTile - 1) / ((int64_t)kBuildTile);
+    if (g.blocks > 0) e = launch_build_scan(g, st);  // the block prefixes again (same values)
+    const uint64_t nt = (uint64_t)(g.s1 - g.s0);
+    g.bucket_base = s.bucket_base;
+    g.n_buckets = s.n_buckets;
+    g.rowref_base = s.rowref_base;
+    g.tail_from = nt ? ((nt - 1) + (uint64_t)lastm[t]) / kKeysPerBucket + 1 : 0;
+    g.tail_value = (uint32_t)(t + 1 < T->n_tables ? T->sub[t + 1].rowref_base : rr);
+    if (e == hipSuccess) e = launch_build_place(g, st);
+  }
+  order.resize(N);
+  unsigned long long disp[2] = {0, 0};
+  if (e == hipSuccess && N) e = hipMemcpyAsync(order.data(), a.sv, 4 * N, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(disp, a.disp, 16, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "device layout build (place)");
+  disp_sum = (double)disp[0];
+  T->max_disp = disp[1];
+  d_buckets = a.buckets;
+  return EMB_OK;
+}
+
+int create_impl(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys, const void* rows,
+                const float* acc, const float* master, const DevBuild* db, EmbTable** out);
+}  // namespace
+
 int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys,
                                const void* rows, const float* acc, const float* master,
                                EmbTable** out) {
+  return create_impl(desc, keys, n_keys, rows, acc, master, nullptr, out);
+}
+
+int table_build_workspace_bytes(const EmbTableDesc* desc, int64_t n_keys, size_t* bytes) {
+  if (!desc || !bytes) return fail(EMB_EINVAL, "null argument");
+  if (n_keys < 0 || n_keys >= (1ll << 31)) return fail(EMB_ERANGE, "the device build takes fewer than 2^31 keys");
+  if (!(desc->load_factor > 0.0 && desc->load_factor <= 1.0))
+    return fail(EMB_EINVAL, "load_factor must be in (0, 1]");
+  if (desc->n_fields < 1 || desc->n_fields > kMaxFields) return fail(EMB_EINVAL, "n_fields must be in [1, 65535]");
+  const int nt = desc->n_tables == 2 ? 2 : 1;
+  *bytes = plan_build(n_keys, bucket_bound(n_keys, desc->load_factor, nt), desc->n_fields).bytes;
+  return EMB_OK;
+}
+
+int table_create_on_device(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys,
+                           void* d_ws, size_t ws_bytes, emb_stream_t stream, EmbTable** out) {
+  if (!d_ws || reinterpret_cast<uintptr_t>(d_ws) % 256)
+    return fail(EMB_EINVAL, "workspace must be non-null and 256-byte aligned");
+  if (n_keys >= (1ll << 31)) return fail(EMB_ERANGE, "the device build takes fewer than 2^31 keys");
+  DevBuild db{static_cast<uint8_t*>(d_ws), ws_bytes, static_cast<hipStream_t>(stream)};
+  return create_impl(desc, keys, n_keys, nullptr, nullptr, nullptr, &db, out);
+}
+
+namespace {
+int create_impl(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys, const void* rows,
+                const float* acc, const float* master, const DevBuild* db, EmbTable** out) {
   if (!desc || !out) return fail(EMB_EINVAL, "null descriptor or output pointer");
   *out = nullptr;
   if (desc->n_fields < 1 || desc->n_fields > kMaxFields)
@@ -496,9 +675,15 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
     const double nh = std::ceil((double)s.n_keys / T->lf);
     if (nh > 4294967295.0 - 64) return fail(EMB_ERANGE, "too many home slots for one table");
     s.n_home = std::max<uint64_t>(1, (uint64_t)nh);
-    ent[t].resize(s.n_keys);
+    if (!db) ent[t].resize(s.n_keys);
   }
-  {
+  std::vector<uint32_t> dev_order;   // device build: caller index of each key in rowref order
+  uint64_t* d_buckets = nullptr;
+  if (db) {
+    const int rc = device_layout(T, K, N, *db, dev_order, d_buckets, disp_sum);
+    if (rc) return rc;
+    rr_total = T->rowref_space;
+  } else {
     size_t p0 = 0, p1 = 0;
     for (size_t i = 0; i < N; ++i) {
       const int t = (T->n_tables == 2 && (K[i] & 1)) ? 1 : 0;
@@ -506,7 +691,6 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
       en.key = K[i];
       en.idx = (uint32_t)i;
     }
-  }
   for (int t = 0; t < T->n_tables; ++t) {
     EmbTable::Sub& s = T->sub[t];
     std::vector<Entry>& E = ent[t];
@@ -535,6 +719,7 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
     for (const Entry& en : E) rr_total += (uint64_t)T->gran[(int)(en.key >> 48)];
     if (rr_total >= 0xFFFFFFFFull) return fail(EMB_ERANGE, "rowref space exceeds 32 bits");
   }
+  }  // host layout
   T->rowref_space = (uint32_t)rr_total;
   // width classes: log2 of the 16-byte lanes a row takes; the backward sorts mixed-width tables
   // by (class, rowref) when the classes fit above the rowref bits and the first radix digit
@@ -586,14 +771,64 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
     (void)madvise(T->image, bytes, MADV_HUGEPAGE);  // advice only; ignored where THP is off
   }
 
+  // the alignment gaps between regions and the tail pad hold zeros, so the image (and every
+  // arena flashed from it) is a pure function of the table's contents
+  {
+    const size_t eb0 = T->elem_bytes, E = T->total_elems;
+    const size_t ends[7][2] = {
+        {T->total_buckets * 128, T->off_rows},
+        {T->off_rows + E * eb0, T->off_acc},
+        {T->off_acc + E * 4, T->off_master},
+        {T->off_master + (T->has_master ? E * 4 : 0), T->off_linear},
+        {T->off_linear + (T->ftrl ? E * 4 : 0), T->off_meta},
+        {T->off_meta + 16 * (size_t)T->F, T->off_touched},
+        {T->off_touched + 4 * T->touched_words, T->arena_bytes}};
+    for (const auto& g : ends)
+      if (g[1] > g[0]) std::memset(T->image + g[0], 0, g[1] - g[0]);
+  }
   // key buckets with per-bucket rowref prefix; per key its rowref
   uint64_t* KB = T->keys_img();
+  T->row_keys.resize(N);
+  T->row_ref.resize(N);
+  std::vector<uint32_t> idx_by_row;
+  if (db) {
+    // the device built the buckets; rowrefs are the running sum of row units in rowref order
+    hipError_t e = hipMemcpyAsync(KB, d_buckets, 128 * (size_t)T->total_buckets,
+                                  hipMemcpyDeviceToHost, db->st);
+    if (e == hipSuccess) e = hipStreamSynchronize(db->st);
+    if (e != hipSuccess) return hip_fail(e, "device layout build (bucket copy)");
+    idx_by_row.swap(dev_order);
+    const int nt = std::max(1, std::min(n_threads(), (int)(N >> 16)));
+    const size_t chunk = (N + nt - 1) / nt;
+    std::vector<uint64_t> part((size_t)nt + 1, 0);
+    std::vector<std::thread> th;
+    for (int c = 0; c < nt; ++c)
+      th.emplace_back([&, c] {
+        uint64_t u = 0;
+        for (size_t r = (size_t)c * chunk; r < std::min(N, (size_t)(c + 1) * chunk); ++r) {
+          const uint64_t k = K[idx_by_row[r]];
+          T->row_keys[r] = k;
+          u += (uint64_t)T->gran[(int)(k >> 48)];
+        }
+        part[(size_t)c + 1] = u;
+      });
+    for (auto& x : th) x.join();
+    th.clear();
+    for (int c = 0; c < nt; ++c) part[(size_t)c + 1] += part[(size_t)c];
+    for (int c = 0; c < nt; ++c)
+      th.emplace_back([&, c] {
+        uint64_t u = part[(size_t)c];
+        for (size_t r = (size_t)c * chunk; r < std::min(N, (size_t)(c + 1) * chunk); ++r) {
+          T->row_ref[r] = (uint32_t)u;
+          u += (uint64_t)T->gran[(int)(T->row_keys[r] >> 48)];
+        }
+      });
+    for (auto& x : th) x.join();
+  } else {
   parallel_for(T->total_buckets * kWordsPerBucket, [&](size_t b, size_t e) {
     std::fill(KB + b, KB + e, kEmpty);
   });
-  T->row_keys.resize(N);
-  T->row_ref.resize(N);
-  std::vector<uint32_t> idx_by_row(N);
+  idx_by_row.resize(N);
   size_t rpos = 0;
   for (int t = 0; t < T->n_tables; ++t) {
     EmbTable::Sub& s = T->sub[t];
@@ -616,6 +851,7 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
     std::vector<Entry>().swap(ent[t]);
     std::vector<uint64_t>().swap(slot_of[t]);
   }
+  }  // host layout
   T->row_of_key.resize(N);
   parallel_for(N, [&](size_t b, size_t e) {
     for (size_t r = b; r < e; ++r) T->row_of_key[idx_by_row[r]] = (uint32_t)r;
@@ -670,6 +906,7 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
   *out = guard.release();
   return EMB_OK;
 }
+}  // namespace
 
 int table_info(const EmbTable* t, EmbTableInfo* info) {
   if (!t || !info) return fail(EMB_EINVAL, "null argument");

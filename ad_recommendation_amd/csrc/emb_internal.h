@@ -173,6 +173,45 @@ struct BwdPlan {
 BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t row_f16,
                  int32_t classed);
 
+// Layout build on the device: the ordered linear-probing layout of the host builder, computed by a
+// radix sort of (table offset + home, caller index), a run-local sort of equal homes by key, a
+// prefix-max scan for the slots (slot_i = i + max_{j<=i}(home_j - j) within a table) and a prefix
+// sum of row units for the rowrefs.
+constexpr int kBuildIpt = 8;
+constexpr int kBuildTile = 256 * kBuildIpt;  // items per block of the build's scans
+struct BuildArgs {
+  const uint64_t* keys;    // [n] keys in the caller's order
+  int64_t n;
+  int32_t n_tables;
+  uint32_t n_home0, n_home1;
+  uint32_t* skey;          // [n] sort keys: home, plus n_home0 for table 1
+  uint32_t* sval;          // [n] caller indices
+  uint32_t* dup;           // [1] set when two keys are equal
+  const int32_t* gran;     // [F] rowref units per row of each field
+  // one table's segment [s0, s1) of the sorted order
+  const uint32_t* sk;      // sorted sort keys
+  uint32_t* sv;            // sorted caller indices (equal homes reordered by key in place)
+  int64_t s0, s1;
+  uint32_t home_base;      // the table's offset inside the sort keys
+  int64_t* bmax;           // [blocks + 1] per block max of (home - local index) -> exclusive prefix max
+  uint32_t* bsum;          // [blocks + 1] per block row units -> exclusive prefix sum
+  int64_t blocks;
+  uint64_t* buckets;       // bucket words of every table
+  uint64_t bucket_base, n_buckets;
+  uint32_t rowref_base;
+  unsigned long long* disp;  // [2] sum and max of (slot - home)
+  uint64_t tail_from;      // prefix words [tail_from, n_buckets) of the table get tail_value
+  uint32_t tail_value;
+};
+hipError_t launch_build_homes(const BuildArgs& a, hipStream_t st);
+// Radix sort of (skey, sval) over key_bits bits with plan p's buffers at ws; returns the sorted
+// arrays (inside ws).
+hipError_t launch_build_sort(const BuildArgs& a, const BwdPlan& p, uint8_t* ws, uint32_t** ks,
+                             uint32_t** vs, hipStream_t st);
+hipError_t launch_build_ties(const BuildArgs& a, hipStream_t st);
+hipError_t launch_build_scan(const BuildArgs& a, hipStream_t st);   // bmax, bsum and their scans
+hipError_t launch_build_place(const BuildArgs& a, hipStream_t st);  // keys, prefix words, tail
+
 // Launchers (emb_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx);
 hipError_t launch_sparse_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ctx);

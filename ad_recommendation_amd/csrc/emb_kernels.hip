@@ -1269,6 +1269,222 @@ int log2_group(int dmax, int epl) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- layout build on the device
+static_assert(kBuildTile == kBlock * kBuildIpt, "build tile");
+__device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int d) {
+  const int lo = __shfl_up((int)(uint32_t)(uint64_t)v, d, 64);
+  const int hi = __shfl_up((int)((uint64_t)v >> 32), d, 64);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+__device__ __forceinline__ int64_t shfl_xor_i64(int64_t v, int d) {
+  const int lo = __shfl_xor((int)(uint32_t)(uint64_t)v, d, 64);
+  const int hi = __shfl_xor((int)((uint64_t)v >> 32), d, 64);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+// Exclusive block-wide (max, sum) scan of one (m, u) pair per thread; totals returned by reference.
+__device__ __forceinline__ void block_excl_maxsum(int64_t m, uint32_t u, int64_t& m_pre, uint32_t& u_pre,
+                                                  int64_t& m_tot, uint32_t& u_tot, int64_t* s_m,
+                                                  uint32_t* s_u) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int64_t mi = m;
+  uint32_t ui = u;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t om = shfl_up_i64(mi, d);
+    const uint32_t ou = __shfl_up(ui, d, 64);
+    if (lane >= d) {
+      mi = om > mi ? om : mi;
+      ui += ou;
+    }
+  }
+  if (lane == 63) {
+    s_m[w] = mi;
+    s_u[w] = ui;
+  }
+  __syncthreads();
+  int64_t wm = INT64_MIN, tm = INT64_MIN;
+  uint32_t wu = 0, tu = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int64_t x = s_m[i];
+    const uint32_t y = s_u[i];
+    if (i < w) {
+      wm = x > wm ? x : wm;
+      wu += y;
+    }
+    tm = x > tm ? x : tm;
+    tu += y;
+  }
+  __syncthreads();
+  int64_t pm = shfl_up_i64(mi, 1);
+  uint32_t pu = __shfl_up(ui, 1, 64);
+  if (lane == 0) {
+    pm = INT64_MIN;
+    pu = 0;
+  }
+  m_pre = pm > wm ? pm : wm;
+  u_pre = pu + wu;
+  m_tot = tm;
+  u_tot = tu;
+}
+
+__global__ __launch_bounds__(kBlock) void k_build_homes(BuildArgs a) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < a.n;
+       i += (int64_t)gridDim.x * kBlock) {
+    const uint64_t k = a.keys[i];
+    const bool t1 = a.n_tables == 2 && (k & 1ull);
+    const uint32_t h = home_slot(mix64(k), t1 ? a.n_home1 : a.n_home0);
+    a.skey[i] = t1 ? a.n_home0 + h : h;
+    a.sval[i] = (uint32_t)i;
+  }
+}
+
+// Runs of equal sort keys (one home) are short; the thread at each run's start orders the run by
+// key (insertion sort) and flags equal keys.
+__global__ __launch_bounds__(kBlock) void k_build_ties(BuildArgs a) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < a.n;
+       i += (int64_t)gridDim.x * kBlock) {
+    const uint32_t h = a.sk[i];
+    if (i > 0 && a.sk[i - 1] == h) continue;
+    int64_t j = i + 1;
+    while (j < a.n && a.sk[j] == h) ++j;
+    if (j - i < 2) continue;
+    for (int64_t p = i + 1; p < j; ++p) {
+      const uint32_t v = a.sv[p];
+      const uint64_t k = a.keys[v];
+      int64_t q = p - 1;
+      while (q >= i && a.keys[a.sv[q]] > k) {
+        a.sv[q + 1] = a.sv[q];
+        --q;
+      }
+      a.sv[q + 1] = v;
+    }
+    for (int64_t p = i + 1; p < j; ++p)
+      if (a.keys[a.sv[p]] == a.keys[a.sv[p - 1]]) atomicOr(a.dup, 1u);
+  }
+}
+
+__device__ __forceinline__ uint32_t build_units(const BuildArgs& a, int64_t i) {
+  return (uint32_t)a.gran[(int)(a.keys[a.sv[i]] >> 48)];
+}
+
+// Per block of kBlock x kBuildIpt items of the segment: max of (home - local index), row units.
+__global__ __launch_bounds__(kBlock) void k_build_blocks(BuildArgs a) {
+  __shared__ int64_t s_m[kWaves];
+  __shared__ uint32_t s_u[kWaves];
+  const int64_t i0 = a.s0 + ((int64_t)blockIdx.x * kBlock + threadIdx.x) * kBuildIpt;
+  int64_t m = INT64_MIN;
+  uint32_t u = 0;
+#pragma unroll
+  for (int q = 0; q < kBuildIpt; ++q) {
+    const int64_t i = i0 + q;
+    if (i < a.s1) {
+      const int64_t v = (int64_t)(a.sk[i] - a.home_base) - (i - a.s0);
+      m = v > m ? v : m;
+      u += build_units(a, i);
+    }
+  }
+  int64_t mp, mt;
+  uint32_t up, ut;
+  block_excl_maxsum(m, u, mp, up, mt, ut, s_m, s_u);
+  if (threadIdx.x == 0) {
+    a.bmax[blockIdx.x] = mt;
+    a.bsum[blockIdx.x] = ut;
+  }
+}
+
+// One block: exclusive prefix max / sum over the per-block values; totals at [blocks].
+__global__ __launch_bounds__(kBlock) void k_build_bscan(BuildArgs a) {
+  __shared__ int64_t s_m[kWaves];
+  __shared__ uint32_t s_u[kWaves];
+  int64_t cm = INT64_MIN;
+  uint32_t cu = 0;
+  for (int64_t c0 = 0; c0 < a.blocks; c0 += kBlock) {
+    const int64_t i = c0 + threadIdx.x;
+    const int64_t m = i < a.blocks ? a.bmax[i] : INT64_MIN;
+    const uint32_t u = i < a.blocks ? a.bsum[i] : 0u;
+    int64_t mp, mt;
+    uint32_t up, ut;
+    block_excl_maxsum(m, u, mp, up, mt, ut, s_m, s_u);
+    if (i < a.blocks) {
+      a.bmax[i] = mp > cm ? mp : cm;
+      a.bsum[i] = cu + up;
+    }
+    cm = mt > cm ? mt : cm;
+    cu += ut;
+  }
+  if (threadIdx.x == 0) {
+    a.bmax[a.blocks] = cm;
+    a.bsum[a.blocks] = cu;
+  }
+}
+
+// Slots and rowrefs of the segment's items; each key goes to its bucket word, and each item writes
+// the prefix word of every bucket from the one after its predecessor's up to its own (the rowref
+// of the first key at or after the bucket's start).
+__global__ __launch_bounds__(kBlock) void k_build_place(BuildArgs a) {
+  __shared__ int64_t s_m[kWaves];
+  __shared__ uint32_t s_u[kWaves];
+  const int64_t i0 = a.s0 + ((int64_t)blockIdx.x * kBlock + threadIdx.x) * kBuildIpt;
+  int64_t v[kBuildIpt];
+  uint32_t un[kBuildIpt];
+  int64_t m = INT64_MIN;
+  uint32_t u = 0;
+#pragma unroll
+  for (int q = 0; q < kBuildIpt; ++q) {
+    const int64_t i = i0 + q;
+    v[q] = INT64_MIN;
+    un[q] = 0;
+    if (i < a.s1) {
+      v[q] = (int64_t)(a.sk[i] - a.home_base) - (i - a.s0);
+      un[q] = build_units(a, i);
+    }
+    m = v[q] > m ? v[q] : m;
+    u += un[q];
+  }
+  int64_t mp, mt;
+  uint32_t up, ut;
+  block_excl_maxsum(m, u, mp, up, mt, ut, s_m, s_u);
+  const int64_t cmb = a.bmax[blockIdx.x];
+  int64_t run_m = mp > cmb ? mp : cmb;     // max over the segment's items before this one
+  uint32_t run_u = a.bsum[blockIdx.x] + up;  // row units before this one
+  unsigned long long dsum = 0, dmax = 0;
+#pragma unroll
+  for (int q = 0; q < kBuildIpt; ++q) {
+    const int64_t i = i0 + q;
+    if (i >= a.s1) break;
+    const int64_t local = i - a.s0;
+    const int64_t prev = local > 0 ? (local - 1) + run_m : -1;  // predecessor's slot
+    run_m = v[q] > run_m ? v[q] : run_m;
+    const uint64_t slot = (uint64_t)(local + run_m);
+    const uint32_t rr = a.rowref_base + run_u;
+    run_u += un[q];
+    const uint64_t b = slot / kKeysPerBucket;
+    a.buckets[(a.bucket_base + b) * kWordsPerBucket + (slot - b * kKeysPerBucket)] = a.keys[a.sv[i]];
+    const int64_t bp = prev < 0 ? -1 : (int64_t)((uint64_t)prev / kKeysPerBucket);
+    for (int64_t c = bp + 1; c <= (int64_t)b; ++c)
+      a.buckets[(a.bucket_base + (uint64_t)c) * kWordsPerBucket + 15] = rr;
+    const unsigned long long d = (unsigned long long)(run_m - v[q]);
+    dsum += d;
+    dmax = d > dmax ? d : dmax;
+  }
+  // displacement statistics: one atomic pair per wave
+  for (int o = 32; o >= 1; o >>= 1) {
+    dsum += (unsigned long long)shfl_xor_i64((int64_t)dsum, o);
+    const unsigned long long x = (unsigned long long)shfl_xor_i64((int64_t)dmax, o);
+    dmax = x > dmax ? x : dmax;
+  }
+  if (lane_id() == 0 && dsum + dmax > 0) {
+    atomicAdd(a.disp, dsum);
+    atomicMax(a.disp + 1, dmax);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_build_tail(BuildArgs a) {
+  for (uint64_t b = a.tail_from + (uint64_t)blockIdx.x * kBlock + threadIdx.x; b < a.n_buckets;
+       b += (uint64_t)gridDim.x * kBlock)
+    a.buckets[(a.bucket_base + b) * kWordsPerBucket + 15] = a.tail_value;
+}
+
 // ---------------------------------------------------------------- end-of-PASS write-back
 __global__ __launch_bounds__(kBlock) void k_wb_count(WbLaunch a) {
   __shared__ uint32_t s_c;
@@ -1646,6 +1862,80 @@ hipError_t launch_sparse_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ct
     KTimer tm(ctx, "seg_counts");
     EMB_LAUNCH(tm, k_seg_counts, dim3(1024), blk, 0, ctx.stream, g);
   }
+  return hipGetLastError();
+}
+
+static unsigned grid_for(int64_t n, int64_t cap) {
+  const int64_t b = (n + kBlock - 1) / kBlock;
+  return (unsigned)(b < 1 ? 1 : b > cap ? cap : b);
+}
+
+hipError_t launch_build_homes(const BuildArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_build_homes, dim3(grid_for(a.n, 65536)), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_ties(const BuildArgs& a, hipStream_t st) {
+  if (a.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_build_ties, dim3(grid_for(a.n, 65536)), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_scan(const BuildArgs& a, hipStream_t st) {
+  if (a.blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_build_blocks, dim3((unsigned)a.blocks), dim3(kBlock), 0, st, a);
+  hipLaunchKernelGGL(k_build_bscan, dim3(1), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_place(const BuildArgs& a, hipStream_t st) {
+  if (a.blocks > 0)
+    hipLaunchKernelGGL(k_build_place, dim3((unsigned)a.blocks), dim3(kBlock), 0, st, a);
+  if (a.tail_from < a.n_buckets)
+    hipLaunchKernelGGL(k_build_tail, dim3(grid_for((int64_t)(a.n_buckets - a.tail_from), 65536)),
+                       dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_sort(const BuildArgs& a, const BwdPlan& p, uint8_t* ws, uint32_t** ks,
+                             uint32_t** vs, hipStream_t st) {
+  SortArgs s{};
+  s.counts = reinterpret_cast<uint32_t*>(ws + p.off_counts);
+  s.gsum = reinterpret_cast<uint32_t*>(ws + p.off_gsum);
+  s.groups = p.groups;
+  s.tile_group = p.tile_group;
+  s.tot = reinterpret_cast<uint32_t*>(ws + p.off_tot);
+  s.ctr = reinterpret_cast<uint32_t*>(ws + p.off_ctr);
+  s.n = p.n;
+  s.tiles = p.tiles;
+  s.tile = kBlock * p.ipt;
+  s.rowref_space = 0xFFFFFFFFu;
+  s.bits = p.bits;
+  const int logb = p.bits <= 8 ? 8 : p.bits;
+  uint32_t* ka = reinterpret_cast<uint32_t*>(ws + p.off_ka);
+  uint32_t* va = reinterpret_cast<uint32_t*>(ws + p.off_va);
+  uint32_t* kb = reinterpret_cast<uint32_t*>(ws + p.off_kb);
+  uint32_t* vb = reinterpret_cast<uint32_t*>(ws + p.off_vb);
+  uint32_t *src_k = ka, *src_v = va, *dst_k = kb, *dst_v = vb;
+  LaunchCtx ctx{st, nullptr};
+  KTimer tm(ctx, "build_sort");
+  const dim3 tiles(p.tiles), blk(kBlock), nbins((1u << p.bits) + 1);
+  for (int pass = 0; pass < p.passes && p.n > 0; ++pass) {
+    s.shift = p.bits * pass;
+    s.kin = src_k;
+    s.vin = src_v;
+    s.kout = dst_k;
+    s.vout = dst_v;
+    hipLaunchKernelGGL(k_sort_hist<false>, dim3(p.groups), blk, 0, st, s);
+    hipLaunchKernelGGL(k_sort_scan, nbins, blk, 0, st, s, pass == 0 ? 1 : 0);
+    launch_scatter<false>(s, p.ipt, logb, tiles, st, tm);
+    std::swap(src_k, dst_k);
+    std::swap(src_v, dst_v);
+  }
+  *ks = src_k;
+  *vs = src_v;
+  (void)a;
   return hipGetLastError();
 }
 

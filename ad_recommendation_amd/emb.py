@@ -74,6 +74,9 @@ def lib() -> C.CDLL:
                             C.c_float, _VP, C.c_size_t, _VP, _VP, _VP, _VP],
         "table_fill_linear": [_VP, _I64, _I64, _VP],
         "table_export_linear": [_VP, _VP, _I64, _VP],
+        "table_build_workspace_bytes": [C.POINTER(EmbTableDesc), _I64, C.POINTER(C.c_size_t)],
+        "table_create_on_device": [C.POINTER(EmbTableDesc), _VP, _I64, _VP, C.c_size_t, _VP,
+                                   C.POINTER(_VP)],
         "pass_writeback": [_VP, _VP],
         "writeback_workspace_bytes": [_VP, C.POINTER(C.c_size_t)],
         "pass_writeback_touched": [_VP, _VP, C.c_size_t, C.POINTER(_I64), _VP],
@@ -104,6 +107,7 @@ def exported_symbols():
             "lookup_pool_fwd", "bwd_workspace_bytes", "sparse_adagrad_bwd", "pass_writeback",
             "writeback_workspace_bytes", "pass_writeback_touched", "table_dirty_keys",
             "table_carry_state", "sparse_ftrl_bwd", "table_fill_linear", "table_export_linear",
+            "table_build_workspace_bytes", "table_create_on_device",
             "table_export", "table_fill_state", "table_key_rowref", "table_rowref_keys", "emb_timing_enable",
             "emb_timing_read", "table_destroy", "emb_last_error"]
 
@@ -165,6 +169,35 @@ def table_create_from_prebuilt(field_dim, row_dtype: int, has_master: bool, n_ta
     h = _VP()
     _check(lib().table_create_from_prebuilt(C.byref(d), _hp(keys), int(keys.size), _hp(rows),
                                             _hp(acc), _hp(master), C.byref(h)))
+    return h
+
+
+def _desc(field_dim, row_dtype, has_master, n_tables, load_factor, acc_init, flags):
+    dims = _host(np.asarray(field_dim, dtype=np.int32), np.int32)
+    d = EmbTableDesc(int(dims.size), dims.ctypes.data_as(C.POINTER(C.c_int32)), int(row_dtype),
+                     int(bool(has_master)), int(n_tables), float(load_factor), float(acc_init),
+                     int(flags))
+    return d, dims
+
+
+def table_build_workspace_bytes(field_dim, n_tables: int, load_factor: float, n_keys: int) -> int:
+    d, _keep = _desc(field_dim, EMB_F32, False, n_tables, load_factor, 0.0, 0)
+    n = C.c_size_t()
+    _check(lib().table_build_workspace_bytes(C.byref(d), int(n_keys), C.byref(n)))
+    return n.value
+
+
+def table_create_on_device(field_dim, row_dtype: int, has_master: bool, n_tables: int,
+                           load_factor: float, acc_init: float, keys, ws, flags: int = 0,
+                           stream=None):
+    """The prebuilt table with its layout computed on the GPU (rows zero, acc = acc_init)."""
+    d, _keep = _desc(field_dim, row_dtype, has_master, n_tables, load_factor, acc_init, flags)
+    keys = _host(np.asarray(keys).view(np.int64) if np.asarray(keys).dtype == np.uint64 else keys,
+                 np.int64)
+    h = _VP()
+    _check(lib().table_create_on_device(C.byref(d), _hp(keys), int(keys.size), _dp(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(),
+                                        _stream(stream), C.byref(h)))
     return h
 
 
@@ -333,12 +366,21 @@ class Table:
 
     def __init__(self, field_dim, row_dtype: int, has_master: bool, n_tables: int,
                  load_factor: float, acc_init: float, keys, rows=None, acc=None, master=None,
-                 flags: int = 0):
+                 flags: int = 0, device_ws=None):
+        """device_ws: a device tensor of table_build_workspace_bytes() bytes or more to build
+        the layout on the GPU (rows, acc and master must then be None; fill them afterwards)."""
         self.field_dim = np.asarray(field_dim, dtype=np.int32)
         self.row_dtype = row_dtype
         self.has_master = bool(has_master)
-        self.h = table_create_from_prebuilt(self.field_dim, row_dtype, has_master, n_tables,
-                                            load_factor, acc_init, keys, rows, acc, master, flags)
+        if device_ws is not None:
+            if rows is not None or acc is not None or master is not None:
+                raise ValueError("the device build takes no state; use fill_state")
+            self.h = table_create_on_device(self.field_dim, row_dtype, has_master, n_tables,
+                                            load_factor, acc_init, keys, device_ws, flags)
+        else:
+            self.h = table_create_from_prebuilt(self.field_dim, row_dtype, has_master, n_tables,
+                                                load_factor, acc_init, keys, rows, acc, master,
+                                                flags)
         self.arena = None
         self.info = table_info(self.h)
 

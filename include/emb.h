@@ -116,6 +116,26 @@ int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, in
                                const void* rows, const float* acc, const float* master,
                                EmbTable** out);
 
+/*
+ * table_create_from_prebuilt(desc, keys, n_keys, NULL, NULL, NULL) with the layout computed on the
+ * GPU: the keys go over to d_ws, are radix-sorted there by (table, home slot) with equal homes
+ * ordered by key, placed by a prefix-max scan (slot_i = max(home_i, slot_{i-1} + 1) is
+ * i + max_{j<=i}(home_j - j)), and their rowrefs come from a prefix sum of row units; the key
+ * buckets and the rowref order come back to the host.  The table, its image and every later
+ * result are identical to the host build's (the pages prepare each PASS's table off the GPU:
+ * Tencent PCG GPU training talk, flash paragraph; this moves the sort, the longest part of that
+ * preparation at 800M keys, onto the GPU).  Rows start at zero and accumulators at acc_init: fill
+ * them with table_fill_state before the first pass_flash.
+ *   d_ws, ws_bytes : device workspace, 256-byte aligned, at least table_build_workspace_bytes()
+ *                    (EMB_ENOSPACE); free again when the call returns.  The arena the table will
+ *                    be flashed into may serve, since nothing is flashed yet.
+ * Synchronises `stream`.  Errors as for table_create_from_prebuilt; n_keys must be below 2^31
+ * (EMB_ERANGE); EMB_EHIP on a failed device call.
+ */
+int table_build_workspace_bytes(const EmbTableDesc* desc, int64_t n_keys, size_t* bytes);
+int table_create_on_device(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys,
+                           void* d_ws, size_t ws_bytes, emb_stream_t stream, EmbTable** out);
+
 /* Sizes and builder statistics of a table (host only). */
 int table_info(const EmbTable* t, EmbTableInfo* info);
 
