@@ -141,6 +141,21 @@ def kernel_bytes(name, st, w, rowref_space, ftrl=False):
     return 0
 
 
+def b_min_bytes(st, w, ftrl=False):
+    """Compulsory bytes of one step: every datum once -- keys in, rowrefs out and back, one bucket
+    hit (key + prefix word) and one row read per distinct row, offsets, pooled output, upstream
+    gradient, and each distinct row's state read and written."""
+    sr = 2 if w.row_dtype == "f16" else 4
+    so = 2 if w.out_dtype == "f16" else 4
+    sg = 2 if w.grad_dtype == "f16" else 4
+    m = 1 if w.has_master else 0
+    ue = st["u_elems_inside"] + st["u_elems_cross"]
+    fwd = st["nnz"] * 12 + st["U"] * 12 + ue * sr + st["bags"] * 4 + st["bag_elems"] * so
+    bwd = (st["bags"] * 4 + st["bag_elems"] * sg + st["nnz"] * 4 +
+           ue * (2 * sr + 8 + 8 * m + (8 if ftrl else 0)))
+    return fwd + bwd
+
+
 def load_traffic(workload, kernel):
     """HBM bytes per launch from rocprofv3 counters, if measured on the current kernel source."""
     try:
@@ -317,6 +332,9 @@ def main():
     ap.add_argument("--optimizer", choices=("adagrad", "ftrl"), default="adagrad",
                     help="sparse update: Adagrad, or FTRL-Proximal (alpha = the workload's lr, "
                          f"beta {FTRL_BETA}, l1 {FTRL_L1}, l2 {FTRL_L2})")
+    ap.add_argument("--flush-mall", action="store_true",
+                    help="also time every kernel with a 512 MB scratch write between steps, so "
+                         "that no step finds the previous one's data in the 256 MB Infinity Cache")
     ap.add_argument("--lifecycle", action="store_true",
                     help="track touched rows (adds the marking kernel to each step) and time the "
                          "end-of-PASS write-backs: touched rows only, then the whole state")
@@ -412,12 +430,30 @@ def main():
         kernels[k] = {"launches_per_step": cnt / R, "ms_per_step": kms / R,
                       "alg_bytes_per_step": float(b), "GB_per_s": float(b / (kms / R) / 1e6)}
     alg_step = sum(v["alg_bytes_per_step"] for v in kernels.values())
+    bmin_step = float(np.mean([b_min_bytes(r["st"], w, ftrl) for r in ring]))
+    ms_fwd = kernels.get("lookup_pool", {}).get("ms_per_step", 0.0)
+    ms_bwd = sum(v["ms_per_step"] for k, v in kernels.items() if k != "lookup_pool")
     log("[bench] per-step kernel time (ms): " +
         ", ".join(f"{k} {v:.4f}" for k, v in sorted(per_step.items(), key=lambda x: -x[1])))
     got_u = n_unique.cpu().numpy()
     want_u = np.array([r["st"]["U"] for r in ring])
     if not np.array_equal(got_u, want_u):
         sys.exit(f"unique-row counts differ from the batches' distinct keys: {got_u} vs {want_u}")
+
+    cold = None
+    if args.flush_mall:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        emb.emb_timing_enable(T.h, True)
+        for i in range(R):
+            scratch.fill_(i & 0xFF)
+            step(i)
+        torch.cuda.synchronize()
+        cc = emb.emb_timing_read(T.h)
+        cold = {"kernels_ms_per_step": {k: v[1] / R for k, v in cc.items()},
+                "ms_per_step": sum(v[1] for v in cc.values()) / R}
+        del scratch
+        log(f"[bench] with the Infinity Cache flushed between steps: {cold['ms_per_step']:.4f} ms "
+            f"of kernels per step")
 
     # timed region: K steps, only the dominant kernel bracketed by events
     emb.emb_timing_enable(T.h, True, dominant)
@@ -501,9 +537,13 @@ def main():
         "cpu_baseline": cpu,
         "pass_flash": flash,
         "pass_writeback": writeback,
+        "cold_cache": cold,
         "step_hbm": {"alg_bytes_per_step": alg_step,
                      "GB_per_s": alg_step / (ms / args.steps) / 1e6,
-                     "frac": alg_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS},
+                     "frac": alg_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS,
+                     "b_min_per_step": bmin_step,
+                     "sol_frac": bmin_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS,
+                     "ms_fwd": ms_fwd, "ms_bwd": ms_bwd},
         "kernels": kernels,
     }
     print(json.dumps(res), flush=True)

@@ -69,3 +69,26 @@ def test_f40_mixed_width_two_tables_full_size_sampled_parity():
     check_sampled(w, keys, bt, res, T.export, rowref_keys=lambda rr: emb.table_rowref_keys(T.h, rr),
                   unique_by_width=bool(T.info["unique_by_width"]))
     T.close()
+
+
+def test_f100_full_size_ftrl_sampled_parity():
+    """The same workload and checks with the FTRL update (alpha = lr, beta 1, l1 0.01, l2 0.1):
+    the table keeps the linear state, and the sampled rows, accumulators, masters and linear
+    states are checked against the oracle's FTRL step."""
+    import bench
+    from tests.test_gpu_parity import gpu_step
+    from tests.test_gpu_pass_scale import check_sampled
+    w = W.F100
+    prm = (w.lr, bench.FTRL_BETA, bench.FTRL_L1, bench.FTRL_L2)
+    t0 = time.perf_counter()
+    T, keys, pinned = bench.build_table(w, extra_flags=emb.FLAG_FTRL)
+    say(f"FTRL table of {keys.size} keys built in {time.perf_counter() - t0:.0f}s (pinned={pinned})")
+    T.flash()
+    torch.cuda.synchronize()
+    bt = synth.batch(w, 0)
+    res = gpu_step(T, bt["keys"], bt["offsets"], bt["grad"], w.out_dtype, w.grad_dtype, 0.0, 0.0,
+                   ftrl=prm)
+    say(f"GPU FTRL step done: {res['n_unique']} unique rows")
+    emb.pass_writeback(T.h)
+    check_sampled(w, keys, bt, res, T.export, ftrl=prm, export_linear=T.export_linear)
+    T.close()

@@ -109,12 +109,14 @@ def test_pass_scale_sampled_parity():
     T.close()
 
 
-def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=False):
+def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=False, ftrl=None,
+                  export_linear=None):
     """The sampled checks on one step's results `res` (as gpu_step returns them) and the state
     after it (`export(keys) -> rows, acc, master`).  One-table fixed-width tables check rowrefs
     against the rank the oracle derives; otherwise `rowref_keys` (the table's rowref -> key map)
     shows that each rowref names the occurrence's key, and `unique_by_width` gives the unique
-    list's order (grouped by width class, ascending within a class)."""
+    list's order (grouped by width class, ascending within a class).  With `ftrl` = (alpha, beta,
+    l1, l2) the step was the FTRL update and `export_linear(keys)` reads the linear state."""
     dims = synth.field_dims(w)
     F = w.n_fields
     simple = w.n_tables == 1 and np.all(dims == dims[0])
@@ -212,14 +214,19 @@ def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=Fa
     del bag_of
     psel = np.searchsorted(want, pick_keys)
     ot = O.Table(pick_keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor,
-                 w.acc_init, P.take(init, roff, psel), master=P.take(init_m, roff, psel))
+                 w.acc_init, P.take(init, roff, psel), master=P.take(init_m, roff, psel),
+                 ftrl=ftrl is not None)
     bud = P.Budget(ot)
     t0 = time.perf_counter()
-    bud.oracle_step(ot, upd_keys, upd_off, bt["grad"], w.lr, w.eps)
+    if ftrl is None:
+        bud.oracle_step(ot, upd_keys, upd_off, bt["grad"], w.lr, w.eps)
+    else:
+        bud.oracle_step_ftrl(ot, upd_keys, upd_off, bt["grad"], *ftrl)
     say(f"oracle update of {pick.size} rows over {upd_keys.size} occurrences in "
         f"{time.perf_counter() - t0:.0f}s")
     rows_g, acc_g, mst_g = export(pick_keys)
-    P.check_state(ot, bud, pick_keys, rows_g, acc_g, mst_g if w.has_master else None)
+    P.check_state(ot, bud, pick_keys, rows_g, acc_g, mst_g if w.has_master else None,
+                  None if ftrl is None else export_linear(pick_keys))
     # untouched resident keys: bit-identical to their initial state
     usel = np.arange(nw, nw + upos.size)
     ru, au, mu = export(keys[upos])
@@ -227,4 +234,6 @@ def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=Fa
     assert ru.tobytes() == P.take(init, roff, usel).tobytes()
     if init_m is not None:
         assert mu.tobytes() == P.take(init_m, roff, usel).tobytes()
+    if ftrl is not None:
+        assert np.all(export_linear(keys[upos]) == 0)
     say(f"{pick.size} updated rows within budget; {upos.size} untouched rows bit-identical")
