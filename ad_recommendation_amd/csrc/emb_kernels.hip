@@ -910,6 +910,7 @@ template <int EPL> struct SegBatch { static constexpr int value = EPL == 4 ? 4 :
 constexpr uint32_t kHeadEnds = 1u, kHeadPasses = 2u;
 
 constexpr int kPieceMax = 256;  // occurrences per update piece, at most
+constexpr int kPieceMin = 192;  // occurrences per update piece, at least (while the batch allows)
 
 // Carries of the segments that cross lane-group boundaries inside a piece, combined once per
 // piece: group g contributes (reset, v, valid) where reset means the carry it passes on does not
@@ -1641,13 +1642,18 @@ BwdPlan plan_bwd(int64_t nnz, uint32_t rowref_space, int32_t max_dim, int32_t ro
   p.off_tot = o; o = al(o + 4 * bins);
   p.off_ctr = o; o = al(o + 4 * 16);
   p.off_seg = o; o = al(o + 4 * ((size_t)p.tiles + 1));
-  // update pieces: about 128k of them (bounded partial traffic), at least one load batch each
+  // update pieces: about 128k of them (bounded partial traffic), and at least kPieceMin
+  // occurrences each.  On the 26-field batch (325k occurrences) pieces of 64, 128, 192 and 256
+  // took the update 26.3, 21.8, 21.0 and 23.4 us on MI355X: small pieces cost more in per-piece
+  // staging and scans than they gain in spread, very large ones leave too few waves.
   const int epl = row_f16 ? 8 : 4;
   p.gsl = log2_group(max_dim, epl);
   const int ipr = 64 >> p.gsl;
   const int br = row_f16 ? SegBatch<8>::value : SegBatch<4>::value;
   int64_t r = (nnz + (int64_t)ipr * 131072 - 1) / ((int64_t)ipr * 131072);
   const int64_t rmax = kPieceMax / ipr;
+  const int64_t rmin = (kPieceMin + ipr - 1) / ipr;
+  r = r < rmin ? rmin : r;
   r = r < br ? br : r > rmax ? rmax : r;
   p.rounds = (int32_t)((r + br - 1) / br * br);
   // mixed-width tables: full pieces, each split among as many lane groups as its rows' width allows

@@ -51,6 +51,7 @@ def piece_plan(nnz, max_dim, row_f16, classed=False):
     ipr = 64 >> gsl
     br = 2 if row_f16 else 4
     r = (nnz + ipr * 131072 - 1) // (ipr * 131072)
+    r = max(r, (192 + ipr - 1) // ipr)   # pieces of at least 192 occurrences
     r = min(max(r, br), 256 // ipr)
     rounds = (r + br - 1) // br * br
     if classed:   # mixed widths sorted by width class: full pieces
