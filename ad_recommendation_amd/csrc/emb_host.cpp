@@ -230,6 +230,11 @@ struct EmbTable {
   // device
   uint8_t* d_arena = nullptr;
   bool flashed = false;
+  // the workspace the last sparse_bwd_dedup sorted, for the one apply call it enables
+  struct Dedup {
+    const void* ws = nullptr;
+    int64_t n_bags = -1, nnz = -1;
+  } dedup;
   Timing timing;
 
   uint64_t* keys_img() { return reinterpret_cast<uint64_t*>(image + off_keys); }
@@ -948,24 +953,31 @@ int pass_flash(EmbTable* t, void* d_arena, size_t arena_bytes, emb_stream_t stre
   if (e != hipSuccess) return hip_fail(e, "pass_flash copy");
   t->d_arena = static_cast<uint8_t*>(d_arena);
   t->flashed = true;
+  t->dedup = EmbTable::Dedup{};  // sorted rowrefs of the previous layout are stale
   return EMB_OK;
 }
 
-int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets, int64_t n_bags,
-                    int64_t nnz, void* d_out, int32_t out_dtype, uint32_t* d_rowref,
-                    int64_t* d_slot, int64_t* d_n_miss, emb_stream_t stream) {
+namespace {
+// The forward: probe and pool in one launch (mode 0), the probe alone (1) or the pooling of
+// earlier rowrefs alone (2).
+int forward(EmbTable* t, int mode, const int64_t* d_keys, const int32_t* d_offsets,
+            int64_t n_bags, int64_t nnz, void* d_out, int32_t out_dtype, uint32_t* d_rowref,
+            int64_t* d_slot, int64_t* d_n_miss, emb_stream_t stream) {
   if (!t) return fail(EMB_EINVAL, "null table");
   if (n_bags < 0 || nnz < 0 || n_bags >= (1ll << 31) || nnz >= (1ll << 31))
     return fail(EMB_EINVAL, "n_bags and nnz must be in [0, 2^31)");
   if (n_bags % t->F) return fail(EMB_EINVAL, "n_bags must be a multiple of n_fields");
-  if (out_dtype != EMB_F32 && out_dtype != EMB_F16) return fail(EMB_EINVAL, "bad out_dtype");
-  if (n_bags > 0 && (!d_offsets || !d_out)) return fail(EMB_EINVAL, "null offsets or output");
+  if (mode != 1 && out_dtype != EMB_F32 && out_dtype != EMB_F16) return fail(EMB_EINVAL, "bad out_dtype");
+  if (n_bags > 0 && !d_offsets) return fail(EMB_EINVAL, "null offsets");
+  if (mode != 1 && n_bags > 0 && !d_out) return fail(EMB_EINVAL, "null output");
   if (nnz > 0 && n_bags == 0) return fail(EMB_EINVAL, "occurrences without bags");
-  if (nnz > 0 && (!d_keys || !d_rowref)) return fail(EMB_EINVAL, "null keys or rowref");
+  if (nnz > 0 && !d_rowref) return fail(EMB_EINVAL, "null rowref");
+  if (mode != 2 && nnz > 0 && !d_keys) return fail(EMB_EINVAL, "null keys");
   if ((reinterpret_cast<uintptr_t>(d_out) | reinterpret_cast<uintptr_t>(d_rowref)) % 16)
     return fail(EMB_EINVAL, "d_out and d_rowref must be 16-byte aligned");
   if (!t->flashed) return fail(EMB_ESTATE, "lookup before pass_flash");
   FwdLaunch a{};
+  a.mode = mode;
   a.d = t->dev();
   a.keys = d_keys;
   a.offsets = d_offsets;
@@ -979,8 +991,30 @@ int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets
   a.probe = (t->flags & EMB_FLAG_PROBE_COOP) ? 1 : (t->flags & EMB_FLAG_PROBE_LANE) ? 2 : 0;
   LaunchCtx ctx{static_cast<hipStream_t>(stream), &t->timing};
   hipError_t e = launch_lookup_pool(a, ctx);
-  if (e != hipSuccess) return hip_fail(e, "lookup_pool_fwd launch");
+  if (e != hipSuccess)
+    return hip_fail(e, mode == 1 ? "lookup_probe launch" : mode == 2 ? "pool_fwd launch" : "lookup_pool_fwd launch");
   return EMB_OK;
+}
+}  // namespace
+
+int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets, int64_t n_bags,
+                    int64_t nnz, void* d_out, int32_t out_dtype, uint32_t* d_rowref,
+                    int64_t* d_slot, int64_t* d_n_miss, emb_stream_t stream) {
+  return forward(t, 0, d_keys, d_offsets, n_bags, nnz, d_out, out_dtype, d_rowref, d_slot,
+                 d_n_miss, stream);
+}
+
+int lookup_probe(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets, int64_t n_bags,
+                 int64_t nnz, uint32_t* d_rowref, int64_t* d_slot, int64_t* d_n_miss,
+                 emb_stream_t stream) {
+  return forward(t, 1, d_keys, d_offsets, n_bags, nnz, nullptr, EMB_F32, d_rowref, d_slot,
+                 d_n_miss, stream);
+}
+
+int pool_fwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets, int64_t n_bags,
+             int64_t nnz, void* d_out, int32_t out_dtype, emb_stream_t stream) {
+  return forward(t, 2, nullptr, d_offsets, n_bags, nnz, d_out, out_dtype,
+                 const_cast<uint32_t*>(d_rowref), nullptr, nullptr, stream);
 }
 
 int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* bytes) {
@@ -992,18 +1026,22 @@ int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* 
 
 namespace {
 // The backward shared by both optimizers: dedup, segmented reduction, fused element-wise update.
-int sparse_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets, int64_t n_bags,
-               int64_t nnz, const void* d_grad, int32_t grad_dtype, float lr, float eps,
-               int ftrl, float beta, float l1, float l2, void* d_ws, size_t ws_bytes,
+// stage 0: dedup and update; 1: dedup only (into the workspace); 2: update of a workspace the
+// last stage-1 call sorted for the same sizes.
+int sparse_bwd(EmbTable* t, int stage, const uint32_t* d_rowref, const int32_t* d_offsets,
+               int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype, float lr,
+               float eps, int ftrl, float beta, float l1, float l2, void* d_ws, size_t ws_bytes,
                uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream) {
   if (!t) return fail(EMB_EINVAL, "null table");
   if (n_bags < 0 || nnz < 0 || n_bags >= (1ll << 31) || nnz >= (1ll << 31))
     return fail(EMB_EINVAL, "n_bags and nnz must be in [0, 2^31)");
   if (n_bags % t->F) return fail(EMB_EINVAL, "n_bags must be a multiple of n_fields");
-  if (grad_dtype != EMB_F32 && grad_dtype != EMB_F16) return fail(EMB_EINVAL, "bad grad_dtype");
+  if (stage != 1 && grad_dtype != EMB_F32 && grad_dtype != EMB_F16) return fail(EMB_EINVAL, "bad grad_dtype");
   if (nnz > 0 && n_bags == 0) return fail(EMB_EINVAL, "occurrences without bags");
-  if (nnz > 0 && (!d_rowref || !d_offsets || !d_grad || !d_ws))
-    return fail(EMB_EINVAL, "null rowref, offsets, grad or workspace");
+  if (nnz > 0 && stage != 2 && (!d_rowref || !d_offsets))
+    return fail(EMB_EINVAL, "null rowref or offsets");
+  if (nnz > 0 && stage != 1 && !d_grad) return fail(EMB_EINVAL, "null grad");
+  if (nnz > 0 && !d_ws) return fail(EMB_EINVAL, "null workspace");
   if (d_count && !d_unique) return fail(EMB_EINVAL, "d_count needs d_unique");
   if ((reinterpret_cast<uintptr_t>(d_grad) | reinterpret_cast<uintptr_t>(d_rowref) |
        reinterpret_cast<uintptr_t>(d_ws)) % 16)
@@ -1015,7 +1053,12 @@ int sparse_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets, 
   if (nnz > 0 && ws_bytes < p.bytes) return fail(EMB_ENOSPACE, "workspace smaller than bwd_workspace_bytes()");
   if (ftrl && !t->ftrl) return fail(EMB_ESTATE, "table keeps no FTRL state (EMB_FLAG_FTRL)");
   if (!t->flashed) return fail(EMB_ESTATE, "backward before pass_flash");
+  if (stage == 2 && (t->dedup.ws != d_ws || t->dedup.nnz != nnz || t->dedup.n_bags != n_bags))
+    return fail(EMB_ESTATE, "apply without a sparse_bwd_dedup of this workspace and these sizes");
+  // a dedup enables one apply; any other backward call may overwrite its workspace
+  t->dedup = EmbTable::Dedup{};
   BwdLaunch a{};
+  a.stage = stage;
   a.d = t->dev();
   a.rowref = d_rowref;
   a.offsets = d_offsets;
@@ -1036,17 +1079,47 @@ int sparse_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets, 
   a.n_unique = d_n_unique;
   LaunchCtx ctx{static_cast<hipStream_t>(stream), &t->timing};
   hipError_t e = launch_sparse_bwd(a, p, ctx);
-  if (e != hipSuccess) return hip_fail(e, ftrl ? "sparse_ftrl_bwd launch" : "sparse_adagrad_bwd launch");
+  if (e != hipSuccess)
+    return hip_fail(e, stage == 1 ? "sparse_bwd_dedup launch"
+                       : ftrl ? "sparse_ftrl_bwd launch" : "sparse_adagrad_bwd launch");
+  if (stage == 1) {
+    t->dedup.ws = d_ws;
+    t->dedup.nnz = nnz;
+    t->dedup.n_bags = n_bags;
+  }
   return EMB_OK;
 }
 }  // namespace
+
+int sparse_bwd_dedup(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                     int64_t n_bags, int64_t nnz, void* d_ws, size_t ws_bytes,
+                     emb_stream_t stream) {
+  return sparse_bwd(t, 1, d_rowref, d_offsets, n_bags, nnz, nullptr, EMB_F32, 0.f, 0.f, 0, 0.f,
+                    0.f, 0.f, d_ws, ws_bytes, nullptr, nullptr, nullptr, stream);
+}
+
+int sparse_adagrad_apply(EmbTable* t, int64_t n_bags, int64_t nnz, const void* d_grad,
+                         int32_t grad_dtype, float lr, float eps, void* d_ws, size_t ws_bytes,
+                         uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique,
+                         emb_stream_t stream) {
+  return sparse_bwd(t, 2, nullptr, nullptr, n_bags, nnz, d_grad, grad_dtype, lr, eps, 0, 0.f,
+                    0.f, 0.f, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
+}
+
+int sparse_ftrl_apply(EmbTable* t, int64_t n_bags, int64_t nnz, const void* d_grad,
+                      int32_t grad_dtype, float alpha, float beta, float l1, float l2, void* d_ws,
+                      size_t ws_bytes, uint32_t* d_unique, int32_t* d_count,
+                      int64_t* d_n_unique, emb_stream_t stream) {
+  return sparse_bwd(t, 2, nullptr, nullptr, n_bags, nnz, d_grad, grad_dtype, alpha, 0.f, 1, beta,
+                    l1, l2, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
+}
 
 int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
                        int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
                        float lr, float eps, void* d_ws, size_t ws_bytes, uint32_t* d_unique,
                        int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream) {
-  return sparse_bwd(t, d_rowref, d_offsets, n_bags, nnz, d_grad, grad_dtype, lr, eps, 0, 0.f, 0.f,
-                    0.f, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
+  return sparse_bwd(t, 0, d_rowref, d_offsets, n_bags, nnz, d_grad, grad_dtype, lr, eps, 0, 0.f,
+                    0.f, 0.f, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
 }
 
 int sparse_ftrl_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
@@ -1054,8 +1127,8 @@ int sparse_ftrl_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offs
                     float alpha, float beta, float l1, float l2, void* d_ws, size_t ws_bytes,
                     uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique,
                     emb_stream_t stream) {
-  return sparse_bwd(t, d_rowref, d_offsets, n_bags, nnz, d_grad, grad_dtype, alpha, 0.f, 1, beta,
-                    l1, l2, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
+  return sparse_bwd(t, 0, d_rowref, d_offsets, n_bags, nnz, d_grad, grad_dtype, alpha, 0.f, 1,
+                    beta, l1, l2, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
 }
 
 int pass_writeback(EmbTable* t, emb_stream_t stream) {
@@ -1142,6 +1215,7 @@ int pass_writeback_touched(EmbTable* t, void* d_ws, size_t ws_bytes, int64_t* n_
   if (!d_ws || reinterpret_cast<uintptr_t>(d_ws) % 256) return fail(EMB_EINVAL, "workspace must be 256-byte aligned");
   const size_t head = wb_head_bytes(t);
   if (ws_bytes < head + 2 * wb_min_half(t)) return fail(EMB_ENOSPACE, "workspace smaller than writeback_workspace_bytes()");
+  t->dedup = EmbTable::Dedup{};  // the workspace may be a deduplicated backward's: it is overwritten
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t ub = wb_unit_bytes(t);
   const bool pin = t->ensure_bounce();

@@ -131,6 +131,7 @@ struct FwdLaunch {
   int64_t* slot;
   unsigned long long* n_miss;
   int32_t probe;  // 0: by bucket-array size, 1: wave-cooperative, 2: per-lane
+  int32_t mode;   // 0: probe and pool, 1: probe only, 2: pool only (rowrefs read from `rowref`)
 };
 
 struct BwdLaunch {
@@ -149,6 +150,7 @@ struct BwdLaunch {
   uint32_t* unique;
   int32_t* count;
   int64_t* n_unique;
+  int32_t stage;         // 0: dedup and update, 1: dedup only, 2: update of a deduped workspace
 };
 
 // Workspace carve-up for the backward (same on host and device side).

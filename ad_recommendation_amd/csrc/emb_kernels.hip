@@ -236,7 +236,8 @@ constexpr int kProbeRounds = 8;  // buckets in flight per lane group: a wave pro
 constexpr uint64_t kCoopProbeBytes = 2ull << 30;
 
 // Gathers and sums the rows of bag jb's occurrences k0..k1 (rowrefs from `rr`), EPL elements per
-// lane, four rows in flight; misses read row 0 and are dropped.
+// lane, four rows in flight; misses (and any rowref outside the table's rowref space) read row 0
+// and are dropped.
 template <typename RowT, typename RR>
 __device__ __forceinline__ typename F32V<16 / sizeof(RowT)>::t pool_rows(const DevDesc& d, RR rr,
                                                                          int k0, int k1, int e0) {
@@ -252,9 +253,9 @@ __device__ __forceinline__ typename F32V<16 / sizeof(RowT)>::t pool_rows(const D
     Raw x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      x[u] = load_raw<RowT, EPL>(rows + (r[u] != kMiss ? (uint64_t)r[u] * d.granule : 0ull));
+      x[u] = load_raw<RowT, EPL>(rows + (r[u] < d.rowref_space ? (uint64_t)r[u] * d.granule : 0ull));
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc += r[u] != kMiss ? to_f32<RowT, EPL>(x[u]) : AccV(0.0f);
+    for (int u = 0; u < 4; ++u) acc += r[u] < d.rowref_space ? to_f32<RowT, EPL>(x[u]) : AccV(0.0f);
   }
   return acc;
 }
@@ -284,7 +285,11 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   const int f0 = (int)((uint32_t)j0 - div_fields(a.d, (uint32_t)j0) * (uint32_t)F);
 
   uint32_t miss = 0;
-  if (!COOP) {
+  if (a.mode == 2) {
+    // pool only: the rowrefs of an earlier probe launch
+    if (in_lds)
+      for (int i = tid; i < nk; i += kBlock) s_rr[i] = a.rowref[base + i];
+  } else if (!COOP) {
     // phase 1, per-lane form: one lane per key
     for (int i = tid; i < nk; i += kBlock) {
       const int32_t pos = base + i;
@@ -398,6 +403,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   if (miss) atomicAdd(&s_miss, miss);
   __syncthreads();
   if (tid == 0 && s_miss && a.n_miss) atomicAdd(a.n_miss, (unsigned long long)s_miss);
+  if (a.mode == 1) return;  // probe only
 
   OutT* out = reinterpret_cast<OutT*>(a.out);
   if (VAR) {
@@ -1585,13 +1591,13 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
   if (a.n_bags <= 0) return hipSuccess;
   const int gs = log2_group(a.d.max_dim, a.d.row_f16 ? 8 : 4);
   const dim3 grid((a.n_bags + kFwdBags - 1) / kFwdBags);
-  KTimer tm(ctx, "lookup_pool");
+  KTimer tm(ctx, a.mode == 1 ? "lookup_probe" : a.mode == 2 ? "pool" : "lookup_pool");
   const dim3 blk(kBlock);
   // the probe form follows the size of the probed bucket array (see the two forms above)
   const uint64_t bucket_bytes =
       ((uint64_t)a.d.tab[0].n_buckets + (a.d.n_tables == 2 ? (uint64_t)a.d.tab[1].n_buckets : 0u)) *
       kWordsPerBucket * 8u;
-  const bool coop = a.probe == 1 || (a.probe == 0 && bucket_bytes >= kCoopProbeBytes);
+  const bool coop = a.mode != 2 && (a.probe == 1 || (a.probe == 0 && bucket_bytes >= kCoopProbeBytes));
 #define EMB_FWD2(R, O, V, C) EMB_LAUNCH(tm, (k_lookup_pool<R, O, V, C>), grid, blk, 0, ctx.stream, a, gs)
 #define EMB_FWD(R, O, V) do { if (coop) EMB_FWD2(R, O, V, true); else EMB_FWD2(R, O, V, false); } while (0)
   if (a.d.row_f16) {
@@ -1705,7 +1711,7 @@ hipError_t launch_sparse_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ct
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.ws);
   uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + p.off_ctr);
   if (p.n <= 0) {
-    if (a.n_unique) {
+    if (a.n_unique && a.stage != 1) {
       KTimer tm(ctx, "set_n_unique");
       EMB_LAUNCH(tm, k_set_i64, dim3(1), dim3(1), 0, ctx.stream, a.n_unique, (int64_t)0);
     }
@@ -1740,7 +1746,14 @@ hipError_t launch_sparse_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ct
   const dim3 tiles(p.tiles), blk(kBlock);
   const dim3 nbins((1u << p.bits) + 1);
   uint32_t *src_k = nullptr, *src_v = nullptr, *dst_k = ka, *dst_v = va;
-  for (int pass = 0; pass < p.passes; ++pass) {
+  if (a.stage == 2) {
+    // the sort ran in an earlier call: its output is where the last of its passes wrote
+    src_k = (p.passes & 1) ? ka : kb;
+    src_v = (p.passes & 1) ? va : vb;
+    dst_k = (p.passes & 1) ? kb : ka;
+    dst_v = (p.passes & 1) ? vb : va;
+  }
+  for (int pass = 0; pass < p.passes && a.stage != 2; ++pass) {
     s.shift = p.bits * pass;
     s.kin = src_k;
     s.vin = src_v;
@@ -1766,7 +1779,7 @@ hipError_t launch_sparse_bwd(const BwdLaunch& a, const BwdPlan& p, LaunchCtx& ct
     dst_v = (src_v == va) ? vb : va;
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || a.stage == 1) return err;
 
   UpdArgs u{};
   u.d = a.d;

@@ -72,6 +72,13 @@ def lib() -> C.CDLL:
                                C.c_size_t, _VP, _VP, _VP, _VP],
         "sparse_ftrl_bwd": [_VP, _VP, _VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float, C.c_float,
                             C.c_float, _VP, C.c_size_t, _VP, _VP, _VP, _VP],
+        "lookup_probe": [_VP, _VP, _VP, _I64, _I64, _VP, _VP, _VP, _VP],
+        "pool_fwd": [_VP, _VP, _VP, _I64, _I64, _VP, _I32, _VP],
+        "sparse_bwd_dedup": [_VP, _VP, _VP, _I64, _I64, _VP, C.c_size_t, _VP],
+        "sparse_adagrad_apply": [_VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float, _VP, C.c_size_t,
+                                 _VP, _VP, _VP, _VP],
+        "sparse_ftrl_apply": [_VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float, C.c_float, C.c_float,
+                              _VP, C.c_size_t, _VP, _VP, _VP, _VP],
         "table_fill_linear": [_VP, _I64, _I64, _VP],
         "table_export_linear": [_VP, _VP, _I64, _VP],
         "table_build_workspace_bytes": [C.POINTER(EmbTableDesc), _I64, C.POINTER(C.c_size_t)],
@@ -107,6 +114,8 @@ def exported_symbols():
             "lookup_pool_fwd", "bwd_workspace_bytes", "sparse_adagrad_bwd", "pass_writeback",
             "writeback_workspace_bytes", "pass_writeback_touched", "table_dirty_keys",
             "table_carry_state", "sparse_ftrl_bwd", "table_fill_linear", "table_export_linear",
+            "lookup_probe", "pool_fwd", "sparse_bwd_dedup", "sparse_adagrad_apply",
+            "sparse_ftrl_apply",
             "table_build_workspace_bytes", "table_create_on_device",
             "table_export", "table_fill_state", "table_key_rowref", "table_rowref_keys", "emb_timing_enable",
             "emb_timing_read", "table_destroy", "emb_last_error"]
@@ -256,6 +265,50 @@ def sparse_ftrl_bwd(h, rowref, offsets, n_bags: int, nnz: int, grad, grad_dtype:
         float(l1), float(l2), _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _dp(unique, (torch.int32,)), _dp(count, (torch.int32,)), _dp(n_unique, (torch.int64,)),
         _stream(stream)))
+
+
+def lookup_probe(h, keys, offsets, n_bags: int, nnz: int, rowref, slot=None, n_miss=None,
+                 stream=None):
+    import torch
+    _check(lib().lookup_probe(
+        h, _dp(keys, (torch.int64,)), _dp(offsets, (torch.int32,)), int(n_bags), int(nnz),
+        _dp(rowref, (torch.int32,)), _dp(slot, (torch.int64,)), _dp(n_miss, (torch.int64,)),
+        _stream(stream)))
+
+
+def pool_fwd(h, rowref, offsets, n_bags: int, nnz: int, out, out_dtype: int, stream=None):
+    import torch
+    _check(lib().pool_fwd(
+        h, _dp(rowref, (torch.int32,)), _dp(offsets, (torch.int32,)), int(n_bags), int(nnz),
+        _dp(out, (torch.float32, torch.float16)), int(out_dtype), _stream(stream)))
+
+
+def sparse_bwd_dedup(h, rowref, offsets, n_bags: int, nnz: int, ws, stream=None):
+    import torch
+    _check(lib().sparse_bwd_dedup(
+        h, _dp(rowref, (torch.int32,)), _dp(offsets, (torch.int32,)), int(n_bags), int(nnz),
+        _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sparse_adagrad_apply(h, n_bags: int, nnz: int, grad, grad_dtype: int, lr: float, eps: float,
+                         ws, unique=None, count=None, n_unique=None, stream=None):
+    import torch
+    _check(lib().sparse_adagrad_apply(
+        h, int(n_bags), int(nnz), _dp(grad, (torch.float32, torch.float16)), int(grad_dtype),
+        float(lr), float(eps), _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _dp(unique, (torch.int32,)), _dp(count, (torch.int32,)), _dp(n_unique, (torch.int64,)),
+        _stream(stream)))
+
+
+def sparse_ftrl_apply(h, n_bags: int, nnz: int, grad, grad_dtype: int, alpha: float, beta: float,
+                      l1: float, l2: float, ws, unique=None, count=None, n_unique=None,
+                      stream=None):
+    import torch
+    _check(lib().sparse_ftrl_apply(
+        h, int(n_bags), int(nnz), _dp(grad, (torch.float32, torch.float16)), int(grad_dtype),
+        float(alpha), float(beta), float(l1), float(l2), _dp(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _dp(unique, (torch.int32,)),
+        _dp(count, (torch.int32,)), _dp(n_unique, (torch.int64,)), _stream(stream)))
 
 
 def table_fill_linear(h, first: int, n: int, z):

@@ -228,6 +228,50 @@ int sparse_ftrl_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offs
                     emb_stream_t stream);
 
 /*
+ * The two halves of each call above, for callers that overlap them on two streams.  The
+ * deduplication of the backward depends only on the rowrefs the probe produced, not on the
+ * gradient (the Tencent PCG talk, "optimisations of each stage", deduplicates a batch's keys
+ * before the update), so it can run on a second stream while the forward pools, or while dense
+ * layers compute, and the update then needs only the gradient.  Each half runs the same kernels
+ * as the fused call, so results are bit-identical to it.
+ *
+ * lookup_probe: the forward's probe alone.  Writes d_rowref (and d_slot, d_n_miss when given)
+ *   exactly as lookup_pool_fwd does and pools nothing.  Arguments and errors as for
+ *   lookup_pool_fwd.
+ * pool_fwd: the forward's pooling alone, of the rowrefs lookup_probe wrote for the same batch
+ *   (d_rowref, d_offsets, n_bags, nnz as given to it, on the same flash).  Writes d_out exactly
+ *   as lookup_pool_fwd does; a rowref at or above the table's rowref space adds nothing, like
+ *   EMB_ROWREF_MISS.  Arguments and errors as for lookup_pool_fwd.
+ * sparse_bwd_dedup: the backward's deduplication alone: sorts the batch's (rowref, bag) pairs
+ *   into d_ws (at least bwd_workspace_bytes(n_bags, nnz) bytes, EMB_ENOSPACE otherwise).  It
+ *   enables one sparse_adagrad_apply or sparse_ftrl_apply call with the same d_ws, n_bags and nnz;
+ *   the workspace must not be used by anything else in between.  Arguments and errors otherwise as
+ *   for sparse_adagrad_bwd.
+ * sparse_adagrad_apply / sparse_ftrl_apply: the reduction and update of sparse_adagrad_bwd /
+ *   sparse_ftrl_bwd from a workspace sparse_bwd_dedup prepared; order them after it on the
+ *   device (same stream, or an event).  EMB_ESTATE when the last backward call on this table was
+ *   not a sparse_bwd_dedup of this d_ws, n_bags and nnz, or a pass_flash or
+ *   pass_writeback_touched came in between.
+ *   Arguments, outputs and other errors as for the fused calls.
+ */
+int lookup_probe(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets, int64_t n_bags,
+                 int64_t nnz, uint32_t* d_rowref, int64_t* d_slot, int64_t* d_n_miss,
+                 emb_stream_t stream);
+int pool_fwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets, int64_t n_bags,
+             int64_t nnz, void* d_out, int32_t out_dtype, emb_stream_t stream);
+int sparse_bwd_dedup(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                     int64_t n_bags, int64_t nnz, void* d_ws, size_t ws_bytes,
+                     emb_stream_t stream);
+int sparse_adagrad_apply(EmbTable* t, int64_t n_bags, int64_t nnz, const void* d_grad,
+                         int32_t grad_dtype, float lr, float eps, void* d_ws, size_t ws_bytes,
+                         uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique,
+                         emb_stream_t stream);
+int sparse_ftrl_apply(EmbTable* t, int64_t n_bags, int64_t nnz, const void* d_grad,
+                      int32_t grad_dtype, float alpha, float beta, float l1, float l2, void* d_ws,
+                      size_t ws_bytes, uint32_t* d_unique, int32_t* d_count,
+                      int64_t* d_n_unique, emb_stream_t stream);
+
+/*
  * Copy rows, accumulators and masters from the device arena back into the table's host image
  * (the end-of-PASS write-back).  Synchronises `stream`.  A pageable image is filled through the
  * same bounce buffers as pass_flash (the DMA of one chunk overlaps the host copy of the other).

@@ -145,6 +145,19 @@ def test_call_errors_without_device_work():
     assert L.sparse_adagrad_bwd(T.h, A, A, 4, 4, A, 0, 0.1, 1e-8, A, 1 << 20, nul, A, nul, nul) == -1  # count w/o unique
     assert L.sparse_adagrad_bwd(T.h, A, A, 4, 4, A + 4, 0, 0.1, 1e-8, A, 1 << 20, nul, nul, nul, nul) == -1  # misaligned grad
     assert L.sparse_adagrad_bwd(T.h, A, A, 4, 4, A, 0, 0.1, 1e-8, A, 1 << 20, nul, nul, nul, nul) == -6
+    # the split halves check the same way
+    assert L.lookup_probe(T.h, nul, A, 4, 4, A, nul, nul, nul) == -1               # null keys
+    assert L.lookup_probe(T.h, A, A, 4, 4, nul, nul, nul, nul) == -1               # null rowref
+    assert L.lookup_probe(T.h, A, A, 4, 4, A, nul, nul, nul) == -6                 # before flash
+    assert L.pool_fwd(T.h, A, A, 4, 4, A, 7, nul) == -1                            # bad out dtype
+    assert L.pool_fwd(T.h, A, A, 4, 4, nul, 0, nul) == -1                          # null output
+    assert L.pool_fwd(T.h, A, A, 4, 4, A, 0, nul) == -6                            # before flash
+    assert L.sparse_bwd_dedup(T.h, A, nul, 4, 4, A, 1 << 20, nul) == -1            # null offsets
+    assert L.sparse_bwd_dedup(T.h, A, A, 4, 4, A, 16, nul) == -5                   # ws too small
+    assert L.sparse_bwd_dedup(T.h, A, A, 4, 4, A, 1 << 20, nul) == -6              # before flash
+    assert L.sparse_adagrad_apply(T.h, 4, 4, nul, 0, 0.1, 1e-8, A, 1 << 20, nul, nul, nul, nul) == -1  # null grad
+    assert L.sparse_adagrad_apply(T.h, 4, 4, A, 0, 0.1, 1e-8, A, 1 << 20, nul, nul, nul, nul) == -6
+    assert L.sparse_ftrl_apply(T.h, 4, 4, A, 0, 0.0, 1.0, 0.0, 0.0, A, 1 << 20, nul, nul, nul, nul) == -1  # alpha 0
     assert L.pass_flash(T.h, 256, 16, nul) == -5                                    # arena too small
     assert L.pass_flash(T.h, 100, 1 << 40, nul) == -1                               # misaligned
     assert L.pass_writeback(T.h, nul) == -6
