@@ -63,6 +63,7 @@ def test_layout_slots_bit_exact_with_oracle(w):
     if w.has_master:
         assert m2.tobytes() == np.concatenate([ot.state_of(int(i))[2] for i in idx]).tobytes()
     assert abs(T.info["mean_displacement"] - (ot.slot - ot.home).mean()) < 1e-9
+    assert T.info["max_displacement"] == int((ot.slot - ot.home).max())
 
 
 def test_absent_keys_miss_on_host_probe():
