@@ -59,7 +59,8 @@ def lib() -> C.CDLL:
     if _LIB is not None:
         return _LIB
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"HIP extension {LIB_PATH} is not built; run __graft_entry__.build()")
+        raise RuntimeError(f"HIP extension {LIB_PATH} is not built; run "
+                           "python -m ad_recommendation_amd.build")
     L = C.CDLL(LIB_PATH)
     sig = {
         "table_create_from_prebuilt": [C.POINTER(EmbTableDesc), _VP, _I64, _VP, _VP, _VP, C.POINTER(_VP)],
