@@ -92,14 +92,18 @@ def batch_stats(w, bt, dims, rowref, classed=False):
         "bag_elems": int(dims.sum()) * (off.size - 1) // F,  # sum of D over bags
         "u_elems_inside": int(uw[~cross].sum()), "u_elems_cross": int(uw[cross].sum()),
         "u_cross": int(cross.sum()), "n_pieces": int(n_pieces), "pdim": int(dims.max()),
+        "classed": bool(classed),
     }
 
 
-def sort_plan(nnz, rowref_space):
-    """Items per thread, tiles and digit bits of the library's radix sort for a batch."""
+def sort_plan(nnz, rowref_space, classed=False):
+    """Items per thread, tiles and digit bits of the library's radix sort for a batch (mixed-width
+    tables carry a 3-bit width class above the rowref bits)."""
     keybits = 0
     while keybits < 32 and rowref_space > 1 and ((rowref_space - 1) >> keybits) != 0:
         keybits += 1
+    if classed:
+        keybits += 3
     maxbits = 9 if nnz >= (4 << 20) else 8
     passes = 1 if keybits <= maxbits else (keybits + maxbits - 1) // maxbits
     bits = (keybits + passes - 1) // passes
@@ -124,7 +128,7 @@ def kernel_bytes(name, st, w, rowref_space, ftrl=False):
     if name == "pool":                                  # the pooling alone: rowref in, row gather
         return n * 4 + st["occ_elems"] * sr + st["bags"] * 4 + st["bag_elems"] * so
     if name in ("sort_hist", "sort_scan", "sort_scatter"):
-        ipt, tiles, bits = sort_plan(n, rowref_space)
+        ipt, tiles, bits = sort_plan(n, rowref_space, st.get("classed", False))
         bins = (1 << bits) + 1                          # digits plus the miss bin
         tile_group = 16 if tiles >= 512 * 16 else tiles // 512 if tiles >= 512 else 1
         groups = (tiles + tile_group - 1) // tile_group

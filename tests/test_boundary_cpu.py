@@ -222,3 +222,27 @@ def test_fill_state_errors():
     with pytest.raises(emb.EmbError) as e:
         T2.fill_state(0, 1, None, None, np.zeros(16, dtype=np.float32))
     assert e.value.name == "EMB_EINVAL"
+
+
+@pytest.mark.parametrize("w", [W.TINY, W.scaled(W.F26, n_keys=300_000, batch=64),
+                               W.scaled(W.F40_VARDIM, n_keys=400_000, batch=64),
+                               W.scaled(W.F100, n_keys=200_000, batch=16)])
+def test_bench_plan_mirrors_the_library(w):
+    """bench.py's byte model re-derives the backward's sort and piece plans; the workspace size
+    those plans imply must equal the library's bwd_workspace_bytes for every batch size."""
+    import bench
+    T, _, _, _ = _table(w)
+    dims = synth.field_dims(w)
+    space, classed = T.info["rowref_space"], bool(T.info["unique_by_width"])
+    al = lambda x: (x + 255) & ~255  # noqa: E731
+    for nnz in (1, 1000, 325_000, 1_500_000, 5_000_000):
+        ipt, tiles, bits = bench.sort_plan(nnz, space, classed)
+        pw, n_pieces = bench.piece_plan(nnz, int(dims.max()), w.row_dtype == "f16", classed)
+        bins = (1 << bits) + 1
+        tg = 16 if tiles >= 512 * 16 else tiles // 512 if tiles >= 512 else 1
+        groups = -(-tiles // tg)
+        npc = max(n_pieces, 1)
+        want = (4 * al(4 * (nnz + 1)) + al(4 * bins * max(tiles, 1)) + al(4 * bins * max(groups, 1))
+                + al(4 * bins) + al(64) + al(4 * (tiles + 1)) + 2 * al(4 * npc * int(dims.max()))
+                + al(4 * npc) + al(8 * npc))
+        assert emb.bwd_workspace_bytes(T.h, w.n_fields, nnz) == want, nnz
