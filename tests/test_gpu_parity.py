@@ -157,6 +157,15 @@ def test_f64_fp16_no_master_scaled():
     run_parity(W.scaled(W.F64_PASS, n_keys=1_000_000, batch=1024), steps=3, check_all_keys=False)
 
 
+def test_f100_mixed_precision_off_scaled():
+    # the JD article's debugging advice (section 5.2): switch mixed precision off to separate fp16
+    # effects from the rest; the 100-field workload with fp32 rows, gradients and output, no master
+    from dataclasses import replace
+    w = replace(W.scaled(W.F100, n_keys=2_000_000, batch=1024, name_suffix="_fp32"),
+                row_dtype="f32", has_master=False, grad_dtype="f32", out_dtype="f32")
+    run_parity(w, steps=3, check_all_keys=False)
+
+
 # ------------------------------------------------------------------ edge cases
 def _edge_batches(w, keys, F):
     """Hand-made CSR batches: empty bags, repeats inside a bag, misses, the EMPTY key, one key
