@@ -243,7 +243,8 @@ int sparse_ftrl_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offs
  *   as lookup_pool_fwd does; a rowref at or above the table's rowref space adds nothing, like
  *   EMB_ROWREF_MISS.  Arguments and errors as for lookup_pool_fwd.
  * sparse_bwd_dedup: the backward's deduplication alone: sorts the batch's (rowref, bag) pairs
- *   into d_ws (at least bwd_workspace_bytes(n_bags, nnz) bytes, EMB_ENOSPACE otherwise).  It
+ *   into d_ws (at least bwd_workspace_bytes(n_bags, nnz) bytes, EMB_ENOSPACE otherwise); a rowref
+ *   at or above the table's rowref space is a miss, as in every backward.  It
  *   enables one sparse_adagrad_apply or sparse_ftrl_apply call with the same d_ws, n_bags and nnz;
  *   the workspace must not be used by anything else in between.  Arguments and errors otherwise as
  *   for sparse_adagrad_bwd.

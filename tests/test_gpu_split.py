@@ -3,7 +3,8 @@ deduplication on a second stream, overlapping the pooling: every output bit-iden
 calls on a twin table over consecutive steps (pooled output, rowrefs, slots, misses, unique rows,
 counts, exported rows, accumulators, masters and linear states), the tiny workload also checked
 against the oracle, and the misuse the host refuses (an apply without its dedup, twice, after a
-flash or a touched write-back, or with other sizes)."""
+flash or a touched write-back, or with other sizes), and caller-made rowrefs outside the table
+acting exactly as misses."""
 import sys
 
 import numpy as np
@@ -219,3 +220,49 @@ def test_touched_writeback_cancels_a_pending_dedup():
     emb.sparse_adagrad_apply(T.h, n_bags, nnz, g, emb.EMB_F32, w.lr, w.eps, ws)
     torch.cuda.synchronize()
     T.close()
+
+
+def test_rowrefs_outside_the_table_count_as_misses():
+    """pool_fwd and sparse_bwd_dedup take rowrefs from the caller: any value at or above the
+    table's rowref space must act exactly like EMB_ROWREF_MISS (the kernels' own bounds checks;
+    nothing outside the rows is read)."""
+    w = W.TINY
+    (A, B), keys, _, _, _ = twin_tables(w)
+    space = int(A.info["rowref_space"])
+    bt = synth.batch(w, 0)
+    dev = "cuda"
+    k = torch.from_numpy(bt["keys"]).to(dev)
+    o = torch.from_numpy(bt["offsets"]).to(dev)
+    g = torch.from_numpy(bt["grad"]).to(dev)
+    n_bags, nnz = o.numel() - 1, k.numel()
+    rowref = torch.empty(nnz, dtype=torch.int32, device=dev)
+    emb.lookup_probe(A.h, k, o, n_bags, nnz, rowref)
+    torch.cuda.synchronize()
+    rr = rowref.cpu().numpy().view(np.uint32).copy()
+    bad = np.array([space, space + 123, 0xFFFFFFFE, 0x80000000], dtype=np.uint32)
+    pos = np.arange(0, nnz, max(1, nnz // 16))[:16]
+    outside, missed = rr.copy(), rr.copy()
+    outside[pos] = bad[np.arange(pos.size) % bad.size]
+    missed[pos] = emb.ROWREF_MISS
+    res = []
+    for T, r in ((A, outside), (B, missed)):
+        rt = torch.from_numpy(r.view(np.int32)).to(dev)
+        out = torch.full((n_bags, 16), float("nan"), dtype=torch.float32, device=dev)
+        emb.pool_fwd(T.h, rt, o, n_bags, nnz, out, emb.EMB_F32)
+        ws = torch.empty(emb.bwd_workspace_bytes(T.h, n_bags, nnz), dtype=torch.uint8, device=dev)
+        uniq = torch.empty(nnz, dtype=torch.int32, device=dev)
+        cnt = torch.empty(nnz, dtype=torch.int32, device=dev)
+        nu = torch.zeros(1, dtype=torch.int64, device=dev)
+        emb.sparse_bwd_dedup(T.h, rt, o, n_bags, nnz, ws)
+        emb.sparse_adagrad_apply(T.h, n_bags, nnz, g, emb.EMB_F32, w.lr, w.eps, ws, uniq, cnt, nu)
+        torch.cuda.synchronize()
+        U = int(nu.item())
+        res.append((out.cpu().numpy(), uniq.cpu().numpy()[:U], cnt.cpu().numpy()[:U]))
+        emb.pass_writeback(T.h)
+    for x, y in zip(res[0], res[1]):
+        assert same_bits(x, y)
+    for x, y in zip(A.export(keys), B.export(keys)):
+        if x is not None or y is not None:
+            assert same_bits(x, y)
+    A.close()
+    B.close()
