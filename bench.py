@@ -28,6 +28,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "embedding rows looked up+updated/sec (fwd+bwd) and achieved HBM GB/s vs peak"
 # FTRL-Proximal hyperparameters besides alpha (the workload's learning rate)
 FTRL_BETA, FTRL_L1, FTRL_L2 = 1.0, 0.01, 0.1
+# largest table the oracle CPU baseline builds (its one-thread build of 50M keys runs for minutes)
+CPU_BASELINE_MAX_KEYS = 5_000_000
 KERNEL_SRC = os.path.join(ROOT, "ad_recommendation_amd", "csrc", "emb_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -280,9 +282,11 @@ def cpu_baseline_child(name: str, min_seconds: float, max_batches: int, optimize
     dims = synth.field_dims(w)
     t0 = time.perf_counter()
     ftrl = optimizer == "ftrl"
+    log(f"[cpu-baseline] building the oracle table of {keys.size} keys (one thread)")
     ot = O.Table(keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor, w.acc_init, rows,
                  master=master, ftrl=ftrl)
     build_s = time.perf_counter() - t0
+    log(f"[cpu-baseline] oracle table built in {build_s:.1f}s; timing its steps")
     t = t_fwd = 0.0
     nnz = n_u = nb = 0
     while nb < max_batches and t < min_seconds:
@@ -319,10 +323,11 @@ def run_cpu_baseline(name: str, optimizer: str = "adagrad"):
     code = ("import os,sys; os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]}); "
             f"sys.path.insert(0, {ROOT!r}); import bench; "
             f"bench.cpu_baseline_child({name!r}, 12.0, 64, {optimizer!r})")
+    # the child's progress lines go straight to this process's stderr
     r = subprocess.run([sys.executable, "-c", code], env=env, stdout=subprocess.PIPE,
-                       stderr=subprocess.PIPE, text=True, timeout=900)
+                       stderr=None, text=True, timeout=900)
     if r.returncode != 0:
-        log(r.stderr[-2000:])
+        log(f"[cpu-baseline] the oracle run failed with status {r.returncode}")
         return None
     return json.loads(r.stdout.strip().splitlines()[-1])
 
@@ -558,7 +563,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        c = run_cpu_baseline(w.name, args.optimizer) if w.n_keys <= 50_000_000 else None
+        # the oracle's single-threaded table build takes minutes beyond a few million keys
+        c = run_cpu_baseline(w.name, args.optimizer) if w.n_keys <= CPU_BASELINE_MAX_KEYS else None
+        if c is None and w.n_keys > CPU_BASELINE_MAX_KEYS:
+            log(f"[cpu-baseline] skipped: {w.n_keys} resident keys is above {CPU_BASELINE_MAX_KEYS}")
         if c:
             cpu = {"value": (c["nnz"] + c["U"]) / c["seconds"], "unit": "rows/s", "cores": 1,
                    "kind": "oracle",
