@@ -246,3 +246,23 @@ def test_bench_plan_mirrors_the_library(w):
                 + al(4 * bins) + al(64) + al(4 * (tiles + 1)) + 2 * al(4 * npc * int(dims.max()))
                 + al(4 * npc) + al(8 * npc))
         assert emb.bwd_workspace_bytes(T.h, w.n_fields, nnz) == want, nnz
+
+
+def test_product_path_never_imports_the_oracle():
+    """The binding and the package load without the oracle (no CPU fallback path exists)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import ad_recommendation_amd; "
+            "from ad_recommendation_amd import emb; emb.lib(); "
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]; "
+            "assert not bad, bad; print('ok')" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
