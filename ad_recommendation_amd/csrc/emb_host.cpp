@@ -222,6 +222,10 @@ struct EmbTable {
   uint8_t* bounce[2] = {nullptr, nullptr};
   hipEvent_t bounce_ev[2] = {nullptr, nullptr};
   bool bounce_tried = false;
+  // probe statistics the forward adds to (device, caller-owned), null when off
+  unsigned long long* probe_stats = nullptr;
+  // EMB_VALIDATE=1: one device word the validation kernel reports into (allocated at first use)
+  uint32_t* d_vflag = nullptr;
   std::vector<uint64_t> row_keys;  // keys in rowref order
   std::vector<uint32_t> row_ref;   // their rowrefs (ascending)
   std::vector<uint32_t> row_of_key;  // position in row_keys of the i-th key given at create
@@ -333,6 +337,7 @@ struct EmbTable {
 
   ~EmbTable() {
     release_bounce();
+    if (d_vflag) (void)hipFree(d_vflag);
     for (auto& r : timing.pool) {
       (void)hipEventDestroy(r.a);
       (void)hipEventDestroy(r.b);
@@ -749,14 +754,19 @@ int create_impl(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys, c
   }
   T->mean_disp = N ? disp_sum / (double)N : 0.0;
 
-  // image layout = arena layout
+  // image layout = arena layout.  On mixed-width tables each state array is followed by one
+  // widest row of zeros: a rowref that names a row narrower than its bag's field (caller-supplied
+  // rowrefs from another batch) then updates elements of the wrong rows, or the pad, but never
+  // the next array or the field metadata the kernels index with.
   const size_t eb = T->elem_bytes;
+  const size_t pad = T->var_dim ? (size_t)T->max_dim : 0;
+  const size_t EP = T->total_elems + pad;
   T->off_keys = 0;
   T->off_rows = align256(T->total_buckets * 128);
-  T->off_acc = align256(T->off_rows + T->total_elems * eb);
-  T->off_master = align256(T->off_acc + T->total_elems * 4);
-  T->off_linear = align256(T->off_master + (T->has_master ? T->total_elems * 4 : 0));
-  T->off_meta = align256(T->off_linear + (T->ftrl ? T->total_elems * 4 : 0));
+  T->off_acc = align256(T->off_rows + EP * eb);
+  T->off_master = align256(T->off_acc + EP * 4);
+  T->off_linear = align256(T->off_master + (T->has_master ? EP * 4 : 0));
+  T->off_meta = align256(T->off_linear + (T->ftrl ? EP * 4 : 0));
   // 4 KiB of tail padding: kernels read row 0 (+ lane offset) in place of a masked-off row, which
   // must stay inside the arena even for an empty table
   T->off_touched = align256(T->off_meta + 4 * 4 * (size_t)T->F);
@@ -958,6 +968,44 @@ int pass_flash(EmbTable* t, void* d_arena, size_t arena_bytes, emb_stream_t stre
 }
 
 namespace {
+bool validate_on() {
+  const char* e = std::getenv("EMB_VALIDATE");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+// EMB_VALIDATE=1: checks a batch on the device before the call uses it -- offsets start at 0,
+// never decrease and end at nnz; with rowrefs, each is a miss or names a whole row of its bag's
+// field -- and synchronises the stream to read the verdict.  EMB_EINVAL names what failed.
+int validate_batch(EmbTable* t, const int32_t* d_offsets, int64_t n_bags, int64_t nnz,
+                   const uint32_t* d_rowref, hipStream_t st) {
+  if (!t->d_vflag) {
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&t->d_vflag), 256);
+    if (e != hipSuccess) {
+      t->d_vflag = nullptr;
+      return hip_fail(e, "EMB_VALIDATE flag allocation");
+    }
+  }
+  ValArgs v{};
+  v.d = t->dev();
+  v.offsets = d_offsets;
+  v.n_bags = (int32_t)n_bags;
+  v.nnz = (int32_t)nnz;
+  v.rowref = nnz > 0 ? d_rowref : nullptr;
+  v.flag = t->d_vflag;
+  hipError_t e = launch_validate(v, st);
+  uint32_t flag = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&flag, t->d_vflag, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "EMB_VALIDATE check");
+  if (flag & 1u) return fail(EMB_EINVAL, "EMB_VALIDATE: offsets[0] is not 0");
+  if (flag & 2u) return fail(EMB_EINVAL, "EMB_VALIDATE: offsets decrease");
+  if (flag & 4u) return fail(EMB_EINVAL, "EMB_VALIDATE: offsets[n_bags] is not nnz");
+  if (flag & 8u)
+    return fail(EMB_EINVAL, "EMB_VALIDATE: a rowref is neither a miss nor a row of its bag's field "
+                            "inside the table");
+  return EMB_OK;
+}
+
 // The forward: probe and pool in one launch (mode 0), the probe alone (1) or the pooling of
 // earlier rowrefs alone (2).
 int forward(EmbTable* t, int mode, const int64_t* d_keys, const int32_t* d_offsets,
@@ -976,6 +1024,11 @@ int forward(EmbTable* t, int mode, const int64_t* d_keys, const int32_t* d_offse
   if ((reinterpret_cast<uintptr_t>(d_out) | reinterpret_cast<uintptr_t>(d_rowref)) % 16)
     return fail(EMB_EINVAL, "d_out and d_rowref must be 16-byte aligned");
   if (!t->flashed) return fail(EMB_ESTATE, "lookup before pass_flash");
+  if (validate_on() && n_bags > 0) {
+    const int rc = validate_batch(t, d_offsets, n_bags, nnz, mode == 2 ? d_rowref : nullptr,
+                                  static_cast<hipStream_t>(stream));
+    if (rc) return rc;
+  }
   FwdLaunch a{};
   a.mode = mode;
   a.d = t->dev();
@@ -989,6 +1042,7 @@ int forward(EmbTable* t, int mode, const int64_t* d_keys, const int32_t* d_offse
   a.slot = d_slot;
   a.n_miss = reinterpret_cast<unsigned long long*>(d_n_miss);
   a.probe = (t->flags & EMB_FLAG_PROBE_COOP) ? 1 : (t->flags & EMB_FLAG_PROBE_LANE) ? 2 : 0;
+  a.stats = mode == 2 ? nullptr : t->probe_stats;
   LaunchCtx ctx{static_cast<hipStream_t>(stream), &t->timing};
   hipError_t e = launch_lookup_pool(a, ctx);
   if (e != hipSuccess)
@@ -1015,6 +1069,13 @@ int pool_fwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets, in
              int64_t nnz, void* d_out, int32_t out_dtype, emb_stream_t stream) {
   return forward(t, 2, nullptr, d_offsets, n_bags, nnz, d_out, out_dtype,
                  const_cast<uint32_t*>(d_rowref), nullptr, nullptr, stream);
+}
+
+int table_probe_stats(EmbTable* t, int64_t* d_stats) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  if (reinterpret_cast<uintptr_t>(d_stats) % 8) return fail(EMB_EINVAL, "d_stats must be 8-byte aligned");
+  t->probe_stats = reinterpret_cast<unsigned long long*>(d_stats);
+  return EMB_OK;
 }
 
 int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* bytes) {
@@ -1055,6 +1116,11 @@ int sparse_bwd(EmbTable* t, int stage, const uint32_t* d_rowref, const int32_t* 
   if (!t->flashed) return fail(EMB_ESTATE, "backward before pass_flash");
   if (stage == 2 && (t->dedup.ws != d_ws || t->dedup.nnz != nnz || t->dedup.n_bags != n_bags))
     return fail(EMB_ESTATE, "apply without a sparse_bwd_dedup of this workspace and these sizes");
+  if (stage != 2 && validate_on() && n_bags > 0) {
+    const int rc = validate_batch(t, d_offsets, n_bags, nnz, d_rowref,
+                                  static_cast<hipStream_t>(stream));
+    if (rc) return rc;
+  }
   // a dedup enables one apply; any other backward call may overwrite its workspace
   t->dedup = EmbTable::Dedup{};
   BwdLaunch a{};

@@ -132,7 +132,24 @@ struct FwdLaunch {
   unsigned long long* n_miss;
   int32_t probe;  // 0: by bucket-array size, 1: wave-cooperative, 2: per-lane
   int32_t mode;   // 0: probe and pool, 1: probe only, 2: pool only (rowrefs read from `rowref`)
+  // probe statistics (null: none): [0] += scans run, [1] += scans that read past the home
+  // bucket, [2] += buckets read, [3] = max(buckets read by one scan)
+  unsigned long long* stats;
 };
+
+// Batch validation (EMB_VALIDATE=1): offsets start at 0, never decrease and end at nnz; with
+// rowrefs, each is a miss or names a whole row of its bag's field.  Bits of *flag: 1 offsets[0],
+// 2 a decrease, 4 the end, 8 a rowref.
+struct ValArgs {
+  DevDesc d;
+  const int32_t* offsets;
+  int32_t n_bags;
+  int32_t nnz;
+  const uint32_t* rowref;  // null: offsets only
+  uint32_t* flag;
+};
+hipError_t launch_validate(const ValArgs& a, hipStream_t st);
+
 
 struct BwdLaunch {
   DevDesc d;

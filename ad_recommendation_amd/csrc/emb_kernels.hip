@@ -125,10 +125,13 @@ __device__ __forceinline__ uint32_t div_fields(const DevDesc& d, uint32_t n) {
 // Two forms.  In the per-lane form below, one lane reads its key's whole bucket (eight 16-byte
 // loads); it needs the least work per key and is the faster one while the table's buckets stay
 // within the reach of the address-translation caches.
+// `nread` receives the buckets the scan read (0 when no scan runs: the EMPTY key, or a key of
+// another field than its bag's).
 template <bool VAR>
 __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, int bag_field,
-                                              int64_t& slot) {
+                                              int64_t& slot, uint32_t& nread) {
   slot = -1;
+  nread = 0;
   if (key == kEmpty || (int)(key >> 48) != bag_field) return kMiss;
   const TabSel tb = pick_tab(d, key);
   const uint32_t home = home_slot(mix64(key), tb.n_home);
@@ -136,6 +139,7 @@ __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, in
   uint32_t l0 = home - b * (uint32_t)kKeysPerBucket;
   for (;;) {
     if (b >= tb.n_buckets) return kMiss;  // unreachable with a well-formed terminator bucket
+    ++nread;
     const u64x2* wp = reinterpret_cast<const u64x2*>(tb.buckets + (uint64_t)b * kWordsPerBucket);
     u64x2 v[8];
 #pragma unroll
@@ -271,12 +275,14 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   __shared__ uint32_t s_pb[kWaves][64];          // their home buckets
   __shared__ uint32_t s_pl[kWaves][64];          // home lane, table, buckets after the home one
   __shared__ uint32_t s_miss;
+  __shared__ uint32_t s_stat[4];                  // probe statistics of the block
   const int tid = threadIdx.x;
   const int32_t j0 = (int32_t)blockIdx.x * kFwdBags;
   const int nb = min(kFwdBags, a.n_bags - j0);
   // offsets are clamped into [0, nnz] so malformed input cannot reach outside the buffers
   for (int i = tid; i <= nb; i += kBlock) s_off[i] = min(max(a.offsets[j0 + i], 0), a.nnz);
   if (tid == 0) s_miss = 0;
+  if (tid < 4) s_stat[tid] = 0;
   __syncthreads();
   const int32_t base = s_off[0];
   const int32_t nk = max(s_off[nb] - base, 0);
@@ -285,6 +291,8 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   const int f0 = (int)((uint32_t)j0 - div_fields(a.d, (uint32_t)j0) * (uint32_t)F);
 
   uint32_t miss = 0;
+  // scans run, scans past the home bucket, buckets read, most buckets one scan read
+  uint32_t st_scan = 0, st_past = 0, st_read = 0, st_max = 0;
   if (a.mode == 2) {
     // pool only: the rowrefs of an earlier probe launch
     if (in_lds)
@@ -302,8 +310,13 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
       int bf = f0 + lo;
       bf = bf >= F ? bf - (int)div_fields(a.d, (uint32_t)bf) * F : bf;
       int64_t sl;
-      const uint32_t rr = probe_key<VAR>(a.d, key, bf, sl);
+      uint32_t nread;
+      const uint32_t rr = probe_key<VAR>(a.d, key, bf, sl, nread);
       miss += (rr == kMiss);
+      st_scan += nread != 0;
+      st_past += nread > 1;
+      st_read += nread;
+      st_max = max(st_max, nread);
       if (in_lds) s_rr[i] = rr;
       a.rowref[pos] = rr;
       if (a.slot) a.slot[pos] = sl;
@@ -380,6 +393,13 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
               if (sub == 0 && i < nk) {
                 const uint32_t rr = key == kEmpty ? kMiss : h.rr;
                 miss += (rr == kMiss);
+                if (key != kEmpty) {
+                  const uint32_t nread = (uint32_t)ext[r] + 1u;
+                  st_scan += 1u;
+                  st_past += nread > 1;
+                  st_read += nread;
+                  st_max = max(st_max, nread);
+                }
                 if (in_lds) s_rr[i] = rr;
                 a.rowref[base + i] = rr;
                 if (a.slot) {
@@ -401,8 +421,20 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
     }
   }
   if (miss) atomicAdd(&s_miss, miss);
+  if (a.stats && st_scan) {
+    atomicAdd(&s_stat[0], st_scan);
+    atomicAdd(&s_stat[1], st_past);
+    atomicAdd(&s_stat[2], st_read);
+    atomicMax(&s_stat[3], st_max);
+  }
   __syncthreads();
   if (tid == 0 && s_miss && a.n_miss) atomicAdd(a.n_miss, (unsigned long long)s_miss);
+  if (tid == 0 && a.stats && s_stat[0]) {
+    atomicAdd(a.stats + 0, (unsigned long long)s_stat[0]);
+    atomicAdd(a.stats + 1, (unsigned long long)s_stat[1]);
+    atomicAdd(a.stats + 2, (unsigned long long)s_stat[2]);
+    atomicMax(a.stats + 3, (unsigned long long)s_stat[3]);
+  }
   if (a.mode == 1) return;  // probe only
 
   OutT* out = reinterpret_cast<OutT*>(a.out);
@@ -1571,6 +1603,42 @@ __global__ __launch_bounds__(kBlock) void k_wb_gather(WbLaunch a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     if (w0 + q < a.n_words && bits[q]) a.touched[w0 + q] = 0u;
+}
+
+// ---------------------------------------------------------------- batch validation
+// One thread per bag: its offsets must not decrease, the first must be 0 and the last nnz; with
+// rowrefs, every occurrence of a well-formed bag must be a miss or start a whole row of the bag's
+// field inside the table (rowref + the field's row units <= rowref space).
+__global__ __launch_bounds__(kBlock) void k_validate(ValArgs a) {
+  uint32_t bad = 0;
+  for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < a.n_bags;
+       j += (int64_t)gridDim.x * kBlock) {
+    const int32_t o0 = a.offsets[j], o1 = a.offsets[j + 1];
+    if (j == 0 && o0 != 0) bad |= 1u;
+    if (o1 < o0) bad |= 2u;
+    if (j == a.n_bags - 1 && o1 != a.nnz) bad |= 4u;
+    if (a.rowref && o0 >= 0 && o1 >= o0 && o1 <= a.nnz) {
+      const int f = (int)(j % a.d.n_fields);
+      const uint64_t units = (uint64_t)a.d.fgran[f];
+      for (int32_t i = o0; i < o1; ++i) {
+        const uint32_t r = a.rowref[i];
+        if (r != kMiss && (uint64_t)r + units > (uint64_t)a.d.rowref_space) bad |= 8u;
+      }
+    }
+  }
+  if (a.n_bags == 0 && a.nnz != 0) bad |= 4u;
+  if (bad) atomicOr(a.flag, bad);
+}
+
+hipError_t launch_validate(const ValArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(64), 0, st, a.flag, 1);
+  if (a.n_bags > 0) {
+    const int64_t b = ((int64_t)a.n_bags + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL(k_validate, dim3((unsigned)(b < 65536 ? b : 65536)), dim3(kBlock), 0, st, a);
+  } else if (a.nnz != 0) {
+    hipLaunchKernelGGL(k_validate, dim3(1), dim3(kBlock), 0, st, a);
+  }
+  return hipGetLastError();
 }
 
 // ================================================================ launchers

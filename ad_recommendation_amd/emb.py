@@ -94,6 +94,7 @@ def lib() -> C.CDLL:
         "table_fill_state": [_VP, _I64, _I64, _VP, _VP, _VP],
         "table_key_rowref": [_VP, _VP, _I64, _VP, _VP],
         "table_rowref_keys": [_VP, _VP, _I64, _VP],
+        "table_probe_stats": [_VP, _VP],
         "emb_timing_enable": [_VP, C.c_int, C.c_char_p],
         "emb_timing_read": [_VP, C.c_char_p, C.c_size_t, _VP, _VP, _I32, C.POINTER(_I32)],
     }
@@ -118,7 +119,8 @@ def exported_symbols():
             "lookup_probe", "pool_fwd", "sparse_bwd_dedup", "sparse_adagrad_apply",
             "sparse_ftrl_apply",
             "table_build_workspace_bytes", "table_create_on_device",
-            "table_export", "table_fill_state", "table_key_rowref", "table_rowref_keys", "emb_timing_enable",
+            "table_export", "table_fill_state", "table_key_rowref", "table_rowref_keys",
+            "table_probe_stats", "emb_timing_enable",
             "emb_timing_read", "table_destroy", "emb_last_error"]
 
 
@@ -237,6 +239,15 @@ def lookup_pool_fwd(h, keys, offsets, n_bags: int, nnz: int, out, out_dtype: int
         h, _dp(keys, (torch.int64,)), _dp(offsets, (torch.int32,)), int(n_bags), int(nnz),
         _dp(out, (torch.float32, torch.float16)), int(out_dtype), _dp(rowref, (torch.int32,)),
         _dp(slot, (torch.int64,)), _dp(n_miss, (torch.int64,)), _stream(stream)))
+
+
+def table_probe_stats(h, stats=None):
+    """Count probe statistics into `stats` (int64 CUDA tensor of 4: scans, scans past the home
+    bucket, buckets read, most buckets of one scan) on every later forward; None stops."""
+    import torch
+    if stats is not None and stats.numel() < 4:
+        raise ValueError("stats needs 4 int64 entries")
+    _check(lib().table_probe_stats(h, _dp(stats, (torch.int64,))))
 
 
 def bwd_workspace_bytes(h, n_bags: int, nnz: int) -> int:

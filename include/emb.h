@@ -26,6 +26,16 @@
  *   - Device work is enqueued on the caller's stream (a hipStream_t passed as void*, NULL = the null
  *     stream) and is asynchronous unless a function says it synchronises.
  *   - A table object is not thread-safe; distinct tables are independent.
+ *   - Batch validation: with the environment variable EMB_VALIDATE=1, every call that takes a
+ *     batch (lookup_pool_fwd, lookup_probe, pool_fwd, sparse_adagrad_bwd, sparse_ftrl_bwd,
+ *     sparse_bwd_dedup) first checks it on the device -- offsets[0] == 0, offsets never
+ *     decrease, offsets[n_bags] == nnz, and for the calls that take rowrefs, each rowref is
+ *     EMB_ROWREF_MISS or names a whole row of its bag's field inside the table -- and returns
+ *     EMB_EINVAL naming the failed check.  The check costs O(nnz) device work, allocates 256
+ *     bytes of device memory once per table and synchronises the stream.  Without it the kernels
+ *     clamp offsets into [0, nnz] and treat rowrefs at or above the table's rowref space as
+ *     misses, so malformed input gives wrong results but no access outside the caller's buffers
+ *     and the table's arena.
  */
 #ifndef MI355EMB_H
 #define MI355EMB_H
@@ -175,6 +185,21 @@ int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets
                     int64_t nnz, void* d_out, int32_t out_dtype, uint32_t* d_rowref,
                     int64_t* d_slot, int64_t* d_n_miss, emb_stream_t stream);
 
+/*
+ * Probe statistics (collision monitoring: the JD ads article, section 4.3, advises watching hash
+ * collisions by sampling the traffic).  While d_stats is set, every lookup_pool_fwd and
+ * lookup_probe of the table adds to four int64 counters on the device, in the same launch:
+ *   d_stats[0] += scans run (occurrences whose key is not the EMPTY marker and whose field is
+ *                 their bag's field; every other occurrence misses without a scan),
+ *   d_stats[1] += scans that read more than the key's home bucket (128 bytes, 15 slots; the home
+ *                 slot h lies in bucket h / 15 and a scan stops at the key or at an empty slot),
+ *   d_stats[2] += buckets read by all scans,
+ *   d_stats[3]  = max(d_stats[3], the most buckets one scan read).
+ * The caller zeroes the counters and reads them when it likes; d_stats = NULL stops the counting.
+ * Host only (no device work); d_stats must be 8-byte aligned (EMB_EINVAL).
+ */
+int table_probe_stats(EmbTable* t, int64_t* d_stats);
+
 /* Device workspace bytes sparse_adagrad_bwd and sparse_ftrl_bwd need for a batch of this shape
  * (host only). */
 int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* bytes);
@@ -187,7 +212,12 @@ int bwd_workspace_bytes(const EmbTable* t, int64_t n_bags, int64_t nnz, size_t* 
  *     fp32 rows: w -= delta;  fp16 rows with master: master -= delta, row = fp16(master);
  *     fp16 rows without master: row = fp16(fp32(row) - delta).
  * Rows, accumulators and masters that no occurrence names are not touched.
- *   d_rowref, d_offsets, n_bags, nnz : as produced for / by lookup_pool_fwd on this flash.
+ *   d_rowref, d_offsets, n_bags, nnz : as produced for / by lookup_pool_fwd on this flash.  The
+ *                rowrefs must be the forward's for these same offsets: a rowref at or above the
+ *                table's rowref space counts as a miss, but on a mixed-width table a rowref
+ *                inside the space that names a narrower row than its bag's field updates
+ *                elements of other rows (the arrays are padded, so nothing outside the table's
+ *                state changes).  EMB_VALIDATE=1 rejects such rowrefs.
  *   d_grad     : upstream gradient, same shape and layout as the forward output, grad_dtype.
  *   d_ws       : workspace of at least bwd_workspace_bytes(n_bags, nnz) (EMB_ENOSPACE); its
  *                contents need no initialisation.

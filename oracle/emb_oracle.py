@@ -333,6 +333,42 @@ class Table:
     def row64(self, i: int) -> np.ndarray:
         return self.rows[self.roff[i]:self.roff[i + 1]].astype(np.float64)
 
+    # ------------------------------------------------------------------ probe statistics
+    def scan_buckets(self, keys: np.ndarray, offsets: np.ndarray, per_bucket: int = 15):
+        """Buckets each occurrence's probe reads, for collision monitoring by sampling (JD
+        article, 4.3).  The probed array is cut into buckets of ``per_bucket`` consecutive slots
+        (slot s lies in bucket s // per_bucket).  A scan runs for every occurrence whose key is
+        not EMPTY and whose field is its bag's field; it starts at the key's home slot and stops
+        at the key, or at the first EMPTY slot at or after home when the key is absent, and
+        reads every bucket from the home slot's to the stop slot's.  Occurrences with no scan
+        read 0 buckets.  Returns int64 [nnz]."""
+        q = np.asarray(keys).view(np.uint64)
+        bag_field = bag_of_occurrence(offsets) % self.F
+        scanned = (q != np.uint64(EMPTY)) & ((q >> np.uint64(FIELD_SHIFT)).astype(np.int64) ==
+                                             bag_field)
+        kidx = self.key_index(q)
+        qt = table_of(q, self.n_tables)
+        out = np.zeros(q.size, dtype=np.int64)
+        for t in range(self.n_tables):
+            sel = np.nonzero(scanned & (qt == t))[0]
+            if sel.size == 0:
+                continue
+            home = home_of(hash64_array(q[sel]), self.n_home[t])
+            occ = np.sort(self.slot[self.tab == t])
+            # last slot of the run of consecutive occupied slots that holds each occupied slot
+            brk = np.nonzero(np.diff(occ) != 1)[0]
+            run_last = np.repeat(occ[np.concatenate([brk, [occ.size - 1]])],
+                                 np.diff(np.concatenate([[-1], brk, [occ.size - 1]]))) \
+                if occ.size else occ
+            p = np.searchsorted(occ, home)
+            pc = np.minimum(p, max(occ.size - 1, 0))
+            inside = (p < occ.size) & (occ[pc] == home) if occ.size else np.zeros(sel.size, bool)
+            first_empty = np.where(inside, run_last[pc] + 1 if occ.size else home, home)
+            hit = kidx[sel] >= 0
+            stop = np.where(hit, self.slot[np.maximum(kidx[sel], 0)], first_empty)
+            out[sel] = stop // per_bucket - home // per_bucket + 1
+        return out
+
     # ------------------------------------------------------------------ forward
     def forward(self, keys: np.ndarray, offsets: np.ndarray, out_dtype: str,
                 bags: Optional[np.ndarray] = None):

@@ -266,3 +266,18 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_mixed_width_state_arrays_are_padded_by_a_widest_row():
+    # each state array of a mixed-width table is followed by one widest row, so a rowref that
+    # names a row narrower than its bag's field cannot reach the next array or the metadata
+    w = W.scaled(W.F40_VARDIM, n_keys=20_000, batch=8)
+    keys = synth.resident_keys(w)
+    dims = synth.field_dims(w)
+    T = emb.Table(dims, emb.EMB_F16, True, w.n_tables, w.load_factor, w.acc_init, keys)
+    E, D = T.info["total_elems"], int(dims.max())
+    # rows (2 B), accumulator (4 B) and master (4 B), each padded, then 256-byte alignment
+    assert T.info["state_bytes"] >= (E + D) * (2 + 4 + 4)
+    F = emb.Table([16] * 4, emb.EMB_F32, False, 1, 0.5, 0.1,
+                  (np.arange(1000, dtype=np.uint64) | (np.uint64(1) << np.uint64(48))))
+    assert F.info["state_bytes"] < (F.info["total_elems"] * 8) + 1024   # fixed width: no pad

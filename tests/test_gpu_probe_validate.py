@@ -1,0 +1,185 @@
+"""GPU tests of two auxiliary parts of the forward and backward calls, through the C ABI.
+
+* Probe statistics (table_probe_stats): scans run, scans past the home bucket, buckets read and
+  the most buckets of one scan, bit-exact against the oracle's per-occurrence bucket counts
+  (Table.scan_buckets) on the same batch, in both probe forms, on workload batches and on edge
+  batches with absent keys, the EMPTY key and keys of another field.
+* Batch validation (EMB_VALIDATE=1): well-formed batches pass and give the same results; offsets
+  that do not start at 0, decrease or do not end at nnz, and rowrefs that name no whole row of
+  their bag's field, are refused with EMB_EINVAL before any kernel uses them.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from ad_recommendation_amd import emb  # noqa: E402
+from gen import synth, workloads as W  # noqa: E402
+from tests import parity_util as P  # noqa: E402
+from tests.test_gpu_parity import DT, TDT, _edge_batches, gpu_table, say  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_stats(ot, keys, offsets):
+    b = ot.scan_buckets(keys, offsets)
+    s = b[b > 0]
+    return [int(s.size), int((s > 1).sum()), int(s.sum()), int(s.max()) if s.size else 0]
+
+
+def gpu_stats(T, w, keys, offsets):
+    dev = "cuda"
+    k = torch.from_numpy(np.ascontiguousarray(keys)).to(dev)
+    o = torch.from_numpy(np.ascontiguousarray(offsets, dtype=np.int32)).to(dev)
+    n_bags, nnz = o.numel() - 1, k.numel()
+    stats = torch.zeros(4, dtype=torch.int64, device=dev)
+    out = torch.empty((n_bags // T.n_fields, T.out_width), dtype=TDT[w.out_dtype], device=dev)
+    rowref = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    emb.table_probe_stats(T.h, stats)
+    emb.lookup_pool_fwd(T.h, k, o, n_bags, nnz, out, DT[w.out_dtype], rowref)
+    emb.lookup_probe(T.h, k, o, n_bags, nnz, rowref)          # the probe alone counts again
+    emb.table_probe_stats(T.h, None)
+    emb.lookup_pool_fwd(T.h, k, o, n_bags, nnz, out, DT[w.out_dtype], rowref)  # not counted
+    torch.cuda.synchronize()
+    s = stats.cpu().numpy().tolist()
+    return [s[0] // 2, s[1] // 2, s[2] // 2, s[3]], s
+
+
+WORKLOADS = [W.TINY, W.scaled(W.F26, n_keys=500_000, batch=1024),
+             W.scaled(W.F40_VARDIM, n_keys=400_000, batch=512),
+             W.scaled(W.F64_PASS, n_keys=600_000, batch=256),
+             W.scaled(W.F100, n_keys=300_000, batch=256, name_suffix="_lf0.6")]
+
+
+@pytest.mark.parametrize("flags", [emb.FLAG_PROBE_LANE, emb.FLAG_PROBE_COOP], ids=["lane", "coop"])
+@pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
+def test_probe_stats_match_oracle(w, flags):
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    dims = synth.field_dims(w)
+    T = gpu_table(w, keys, rows, master, dims, flags)
+    ot = P.oracle_table(w, keys, rows, master, dims)
+    batches = [synth.batch(w, 0)] + _edge_batches(w, keys, w.n_fields)
+    for bt in batches:
+        want = oracle_stats(ot, bt["keys"], bt["offsets"])
+        got, raw = gpu_stats(T, w, bt["keys"], bt["offsets"])
+        say(f"[stats] {w.name}: oracle {want}, gpu {got}")
+        assert raw[0] == 2 * want[0] and raw[1] == 2 * want[1] and raw[2] == 2 * want[2]
+        assert got == want
+    T.close()
+
+
+def test_probe_stats_dense_table_reads_many_buckets():
+    # load factor 1.0: long clusters, so scans leave their home bucket often and the maximum is
+    # large; both forms agree with the oracle
+    from dataclasses import replace
+    w = replace(W.scaled(W.F26, n_keys=300_000, batch=512, name_suffix="_lf1"), load_factor=1.0)
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    dims = synth.field_dims(w)
+    ot = P.oracle_table(w, keys, rows, master, dims)
+    bt = synth.batch(w, 0)
+    want = oracle_stats(ot, bt["keys"], bt["offsets"])
+    assert want[1] > want[0] // 10 and want[3] >= 3
+    for flags in (emb.FLAG_PROBE_LANE, emb.FLAG_PROBE_COOP):
+        T = gpu_table(w, keys, rows, master, dims, flags)
+        got, _ = gpu_stats(T, w, bt["keys"], bt["offsets"])
+        assert got == want
+        T.close()
+
+
+# ------------------------------------------------------------------ EMB_VALIDATE
+def _dev(a, dt=None):
+    return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to("cuda")
+
+
+def test_validate_accepts_good_batches_and_refuses_bad_offsets(monkeypatch):
+    w = W.scaled(W.F26, n_keys=100_000, batch=64)
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    dims = synth.field_dims(w)
+    T = gpu_table(w, keys, rows, master, dims)
+    bt = synth.batch(w, 0)
+    # the same step with and without validation gives the same results
+    from tests.test_gpu_parity import gpu_step
+    ref = gpu_step(T, bt["keys"], bt["offsets"], bt["grad"], "f32", "f32", w.lr, w.eps)
+    T.close()
+    monkeypatch.setenv("EMB_VALIDATE", "1")
+    T = gpu_table(w, keys, rows, master, dims)
+    got = gpu_step(T, bt["keys"], bt["offsets"], bt["grad"], "f32", "f32", w.lr, w.eps)
+    for k in ("out", "rowref", "unique", "count"):
+        assert np.array_equal(got[k], ref[k])
+    k = _dev(bt["keys"])
+    n_bags, nnz = bt["offsets"].size - 1, bt["keys"].size
+    out = torch.empty((w.batch, int(dims.sum())), dtype=torch.float32, device="cuda")
+    rowref = torch.empty(nnz, dtype=torch.int32, device="cuda")
+    ws = torch.empty(emb.bwd_workspace_bytes(T.h, n_bags, nnz), dtype=torch.uint8, device="cuda")
+    g = _dev(bt["grad"])
+    bad = []
+    o = bt["offsets"].copy()
+    o[0] = 1
+    bad.append(("offsets[0]", o))
+    o = bt["offsets"].copy()
+    o[5], o[6] = o[6] + 1, o[6]
+    bad.append(("decrease", o))
+    o = bt["offsets"].copy()
+    o[-1] = nnz - 1
+    bad.append(("offsets[n_bags]", o))
+    for what, o in bad:
+        od = _dev(o, np.int32)
+        with pytest.raises(emb.EmbError) as e:
+            emb.lookup_pool_fwd(T.h, k, od, n_bags, nnz, out, emb.EMB_F32, rowref)
+        assert e.value.name == "EMB_EINVAL" and "EMB_VALIDATE" in str(e.value), what
+        with pytest.raises(emb.EmbError) as e:
+            emb.sparse_bwd_dedup(T.h, rowref, od, n_bags, nnz, ws)
+        assert e.value.name == "EMB_EINVAL", what
+    # rowrefs beyond the table: refused by the backward and by pool_fwd
+    od = _dev(bt["offsets"], np.int32)
+    emb.lookup_probe(T.h, k, od, n_bags, nnz, rowref)
+    rr = rowref.clone()
+    rr[3] = int(T.info["rowref_space"])
+    with pytest.raises(emb.EmbError):
+        emb.pool_fwd(T.h, rr, od, n_bags, nnz, out, emb.EMB_F32)
+    with pytest.raises(emb.EmbError):
+        emb.sparse_adagrad_bwd(T.h, rr, od, n_bags, nnz, g, emb.EMB_F32, w.lr, w.eps, ws)
+    # misses are fine
+    rr[3] = -1
+    emb.pool_fwd(T.h, rr, od, n_bags, nnz, out, emb.EMB_F32)
+    torch.cuda.synchronize()
+    T.close()
+
+
+def test_validate_refuses_rowrefs_of_narrower_rows_on_mixed_widths(monkeypatch):
+    # on a mixed-width table a rowref inside the rowref space may still name a row narrower than
+    # its bag's field (the last row of a narrow field placed in a wide field's bag would reach
+    # past the arrays without the padding); validation refuses it
+    w = W.scaled(W.F40_VARDIM, n_keys=50_000, batch=16)
+    keys = synth.resident_keys(w)
+    rows, master = synth.initial_state(w)
+    dims = synth.field_dims(w)
+    T = gpu_table(w, keys, rows, master, dims)
+    monkeypatch.setenv("EMB_VALIDATE", "1")
+    wide = int(np.argmax(dims))
+    narrow = int(np.argmin(dims))
+    gran = int(T.info["granule"])
+    space = int(T.info["rowref_space"])
+    # the rowref at the very end of the space is one unit: a row of the narrowest width only if
+    # that width is the granule; any rowref within (D_wide / granule - 1) units of the end is
+    # refused for a bag of the widest field
+    F = w.n_fields
+    n_bags = F
+    off = np.zeros(F + 1, dtype=np.int32)
+    off[wide + 1:] = 1
+    od = _dev(off)
+    rr = torch.tensor([space - 1], dtype=torch.int32, device="cuda")
+    out = torch.empty((1, int(dims.sum())), dtype=torch.float16, device="cuda")
+    assert dims[wide] > gran and dims[narrow] < dims[wide]
+    with pytest.raises(emb.EmbError) as e:
+        emb.pool_fwd(T.h, rr, od, n_bags, 1, out, emb.EMB_F16)
+    assert "rowref" in str(e.value)
+    ws = torch.empty(emb.bwd_workspace_bytes(T.h, n_bags, 1), dtype=torch.uint8, device="cuda")
+    g = torch.zeros((1, int(dims.sum())), dtype=torch.float16, device="cuda")
+    with pytest.raises(emb.EmbError):
+        emb.sparse_adagrad_bwd(T.h, rr, od, n_bags, 1, g, emb.EMB_F16, w.lr, w.eps, ws)
+    torch.cuda.synchronize()
+    T.close()
