@@ -307,3 +307,21 @@ def upstream_grad(w: Workload, b: int) -> np.ndarray:
         e = min(w.batch, s + step)
         g[s:e] = r.standard_normal((e - s, width), dtype=np.float32).astype(dt)
     return g
+
+
+def dyadic_grad(w: Workload, b: int) -> np.ndarray:
+    """An upstream gradient of the pooled output whose every element is a multiple of 2^-7 in
+    [-1, 1] (uniform over the 257 values), in the workload's gradient dtype, where such values are
+    exact.  A sum of up to 2^17 of them needs at most 24 significant bits, so every fp32 partial
+    sum of a row's gradient is exact in any order: the summed gradient of even the hottest row is
+    the same on every side."""
+    width = int(field_dims(w).sum())
+    r = rng_for(w, S_GRADS, 1_000_000 + b)
+    dt = np.float16 if w.grad_dtype == "f16" else np.float32
+    g = np.empty((w.batch, width), dtype=dt)
+    step = max(1, (1 << 24) // max(width, 1))
+    for s in range(0, w.batch, step):
+        e = min(w.batch, s + step)
+        g[s:e] = (r.integers(-128, 129, size=(e - s, width)).astype(np.float32) /
+                  np.float32(128.0)).astype(dt)
+    return g

@@ -1,23 +1,24 @@
-"""Parity at the full PASS scale: 800M resident keys in one unified table (dim 32, fp16 rows,
-fp32 accumulators, ~167 GB in HBM), one batch of 131,072 samples x 64 fields (~50M lookups),
-in the launch configuration the benchmark times.
+"""Parity at the full PASS scale and at an intermediate scale that crosses the same thresholds.
 
-The oracle cannot hold this table, so it checks samples it computes one by one:
-  * slots and rowrefs of 20,000 sampled occurrences, bit-exact, from per-home key counts
-    (``oracle.slots_of_sample``) rather than a sort of all 800M keys;
-  * the pooled output of 1 sample in 64 (all 64 of its bags), within the fp16 tolerance;
-  * the number of distinct rows touched, bit-exact, and the count of sampled unique rows;
-  * rows and accumulators of 1 % of the touched keys after the update, within the derived
-    budgets, and sampled untouched keys bit-identical.
-For the pooled check the oracle is a table over the keys of the sampled samples, fed just those
-samples.  For the update check it is a table over the sampled touched keys, fed the batch with
-every other key's occurrences dropped (all bags and the full upstream gradient kept), which
-leaves those keys' gradient sums as they are.
+* PASS scale: 800M resident keys in one unified table (dim 32, fp16 rows, fp32 accumulators,
+  ~167 GB in HBM), batches of 131,072 samples x 64 fields (~50M lookups), in the launch
+  configuration the benchmark times: the table's layout built on the GPU, the bucket array far
+  above 2 GiB (so the forward takes the wave-cooperative probe by itself), row offsets above 2^32.
+  Two consecutive steps on one table: batch 0 with dyadic upstream gradients (exact fp32 gradient
+  sums, so the hottest rows' accumulators are checked within 2 ulp), then batch 1 with the
+  workload's N(0, 1) fp16 gradients on the state batch 0 left.
+* Intermediate scale: 150M keys of the same shape (2.6 GB of buckets, 4.8G row elements), a
+  batch of 32,768 samples, the same two steps.  It runs wherever the PASS-scale one cannot.
 
-Opt-in (EMB_PASS_SCALE=1): building the table takes minutes and ~200 GB of host memory.
+The checks are the sampled ones of tests/sampled_parity.py: slots and rowrefs of sampled
+occurrences bit-exact, the unique count exact, the hot rows (64 most frequent keys and every key
+whose segment can span more than 64 update pieces) and 1 % of the other touched rows checked for
+counts and state, 1 sample in 64 pooled, sampled untouched rows bit-identical.
+
+The PASS-scale test needs ~210 GB of free host memory and ~180 GB of free device memory; it is
+skipped, saying so, when either is short.
 """
 import os
-import sys
 import time
 
 import numpy as np
@@ -27,213 +28,77 @@ torch = pytest.importorskip("torch")
 
 from ad_recommendation_amd import emb  # noqa: E402
 from gen import synth, workloads as W  # noqa: E402
-from oracle import emb_oracle as O  # noqa: E402
-from tests import parity_util as P  # noqa: E402
+from tests.sampled_parity import SampledRun, say  # noqa: E402
 
-pytestmark = [pytest.mark.gpu,
-              pytest.mark.skipif(os.environ.get("EMB_PASS_SCALE") != "1",
-                                 reason="800M-key table: set EMB_PASS_SCALE=1 (minutes, ~200 GB host)")]
+pytestmark = pytest.mark.gpu
 
-
-def say(*a):
-    print("[pass-scale]", *a, flush=True)
-    sys.stdout.flush()
+PASS_HOST_BYTES = 210 << 30
+PASS_DEVICE_BYTES = 180 << 30
 
 
-def positions(keys, want, chunk=1 << 24):
-    """Index in `keys` of each of the sorted distinct keys `want` (each must occur once), in one
-    pass over `keys` without sorting it."""
-    pos = np.full(want.size, -1, dtype=np.int64)
-    low = np.uint64((1 << 28) - 1)
-    maybe = np.zeros(1 << 28, dtype=bool)            # filter on the low 28 bits first
-    maybe[(want & low).astype(np.intp)] = True
-    for a in range(0, keys.size, chunk):
-        kc = keys[a:a + chunk]
-        c = np.nonzero(maybe[(kc & low).astype(np.intp)])[0]
-        i = np.minimum(np.searchsorted(want, kc[c]), want.size - 1)
-        hit = want[i] == kc[c]
-        pos[i[hit]] = a + c[hit]
-    assert np.all(pos >= 0)
-    return pos
+def host_available() -> int:
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemAvailable:"):
+                return int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return 0
 
 
-def initial_rows(w, pos):
-    """Initial rows (and fp32 master copies, when the workload keeps them) of the resident keys at
-    positions `pos`, packed in that order with each key's field width; each field that holds one
-    of them is regenerated once (fields on a thread pool).
-    Returns (rows, master or None, offsets [n + 1] into both)."""
-    from concurrent.futures import ThreadPoolExecutor
-    dims = synth.field_dims(w).astype(np.int64)
-    foff = synth.field_key_offsets(w)
-    fld = np.searchsorted(foff, pos, side="right") - 1
-    width = dims[fld]
-    roff = np.concatenate([[0], np.cumsum(width)])
-    out = np.empty(int(roff[-1]), dtype=np.float16 if w.row_dtype == "f16" else np.float32)
-    mst = np.empty(int(roff[-1]), dtype=np.float32) if w.has_master else None
-
-    def one(f):
-        sel = np.nonzero(fld == f)[0]
-        if sel.size:
-            D = int(dims[f])
-            r_f, m_f = synth.field_state(w, f)
-            dst = (roff[sel][:, None] + np.arange(D)[None, :]).reshape(-1)
-            src = ((pos[sel] - foff[f])[:, None] * D + np.arange(D)[None, :]).reshape(-1)
-            out[dst] = r_f[src]
-            if mst is not None:
-                mst[dst] = m_f[src]
-    with ThreadPoolExecutor(max(1, min(8, synth.worker_count()))) as ex:
-        list(ex.map(one, range(w.n_fields)))
-    return out, mst, roff
-
-
-def test_pass_scale_sampled_parity():
-    import bench
+def two_steps(w, T, keys, unique_by_width=False):
+    """Batch 0 with dyadic gradients, then batch 1 with the workload's gradients, each checked on
+    samples against the oracle."""
     from tests.test_gpu_parity import gpu_step
-    w = W.F64_PASS
+    b0 = synth.batch(w, 0, with_grad=False)
+    b0["grad"] = synth.dyadic_grad(w, 0)
+    b1 = synth.batch(w, 1)
+    run = SampledRun(w, keys, [b0, b1], classed=bool(T.info["unique_by_width"]),
+                     unique_by_width=unique_by_width,
+                     rowref_keys=lambda rr: emb.table_rowref_keys(T.h, rr))
+    for s, bt in enumerate((b0, b1)):
+        t0 = time.perf_counter()
+        res = gpu_step(T, bt["keys"], bt["offsets"], bt["grad"], w.out_dtype, w.grad_dtype, w.lr,
+                       w.eps)
+        emb.pass_writeback(T.h)
+        say(f"GPU step {s} and write-back in {time.perf_counter() - t0:.1f}s: "
+            f"{res['n_unique']} unique rows, {res['n_miss']} misses")
+        run.after_step(s, res, T.export, exact_grad=(s == 0))
+
+
+def build_flash(w):
+    import bench
     t0 = time.perf_counter()
     T, keys, pinned = bench.build_table(w)
-    say(f"table of {keys.size} keys built and filled in {time.perf_counter() - t0:.0f}s "
-        f"(pinned={pinned}); arena {T.info['arena_bytes'] / 1e9:.1f} GB")
+    info = T.info
+    say(f"{w.name}: table of {keys.size} keys built in {time.perf_counter() - t0:.0f}s "
+        f"(pinned={pinned}); arena {info['arena_bytes'] / 1e9:.1f} GB, buckets "
+        f"{info['key_bytes'] / 2**30:.2f} GiB, {info['total_elems']} row elements")
     t0 = time.perf_counter()
     T.flash()
     torch.cuda.synchronize()
     say(f"flashed in {time.perf_counter() - t0:.1f}s")
-    bt = synth.batch(w, 0)
-    say(f"batch 0: {bt['keys'].size} lookups")
-    res = gpu_step(T, bt["keys"], bt["offsets"], bt["grad"], w.out_dtype, w.grad_dtype, w.lr,
-                   w.eps)
-    say(f"GPU step done: {res['n_unique']} unique rows, {res['n_miss']} misses")
-    emb.pass_writeback(T.h)
-    say("state written back")
-    check_sampled(w, keys, bt, res, T.export)
+    return T, keys
+
+
+def test_intermediate_scale_two_steps():
+    # 150M keys: the cooperative probe is chosen by size (>= 2 GiB of buckets), element offsets
+    # pass 2^32 and the layout is built on the GPU, at a third of the PASS-scale table's memory
+    w = W.scaled(W.F64_PASS, n_keys=150_000_000, batch=32_768, name_suffix="_k150m")
+    T, keys = build_flash(w)
+    assert T.info["key_bytes"] >= 2 << 30 and T.info["total_elems"] > 1 << 32
+    two_steps(w, T, keys)
     T.close()
 
 
-def check_sampled(w, keys, bt, res, export, rowref_keys=None, unique_by_width=False, ftrl=None,
-                  export_linear=None):
-    """The sampled checks on one step's results `res` (as gpu_step returns them) and the state
-    after it (`export(keys) -> rows, acc, master`).  One-table fixed-width tables check rowrefs
-    against the rank the oracle derives; otherwise `rowref_keys` (the table's rowref -> key map)
-    shows that each rowref names the occurrence's key, and `unique_by_width` gives the unique
-    list's order (grouped by width class, ascending within a class).  With `ftrl` = (alpha, beta,
-    l1, l2) the step was the FTRL update and `export_linear(keys)` reads the linear state."""
-    dims = synth.field_dims(w)
-    F = w.n_fields
-    simple = w.n_tables == 1 and np.all(dims == dims[0])
-    bkeys = bt["keys"].view(np.uint64)
-    nnz = bkeys.size
-    assert res["n_miss"] == 0
-    r = np.random.default_rng(7)
-    bk, bcount = np.unique(bkeys, return_counts=True)
-    assert res["n_unique"] == bk.size
-    uq = res["unique"].astype(np.int64)
-    if unique_by_width:
-        epl = 8 if w.row_dtype == "f16" else 4
-        wcls = np.ceil(np.log2(-(-dims.astype(np.int64) // epl))).astype(np.int64)
-        ucls = wcls[(rowref_keys(res["unique"]).view(np.uint64) >> np.uint64(48)).astype(np.int64)]
-        assert np.all(np.diff(ucls) >= 0)
-        assert np.all(np.diff(uq)[np.diff(ucls) == 0] > 0)
-    else:
-        assert np.all(np.diff(uq) > 0)
-    # samples: occurrences (slots), 1 % of touched keys (counts, update), 1 sample in 64 with
-    # all of its bags (pooling)
-    occ = np.unique(r.integers(0, nnz, size=20_000))
-    pick = np.unique(r.integers(0, bk.size, size=max(1, bk.size // 100)))
-    pick_keys = bk[pick]
-    off64 = bt["offsets"].astype(np.int64)
-    lens = np.diff(off64)
-    samp = np.arange(0, w.batch, 64)
-    bag_ids = (samp[:, None] * F + np.arange(F)[None, :]).reshape(-1)
-    sl = lens[bag_ids]
-    sub_off = np.concatenate([[0], np.cumsum(sl)])
-    sub_idx = np.repeat(off64[bag_ids], sl) + (np.arange(sub_off[-1]) - np.repeat(sub_off[:-1], sl))
-    sub_keys = bkeys[sub_idx]
-    fwd_keys = np.unique(sub_keys)
-    want = np.unique(np.concatenate([bkeys[occ], pick_keys, fwd_keys]))
-    t0 = time.perf_counter()
-    wpos = positions(keys, want)
-    say(f"{want.size} sampled keys located in {time.perf_counter() - t0:.0f}s")
-    upos = np.unique(r.integers(0, keys.size, size=5000))      # untouched candidates
-    upos = upos[~np.isin(keys[upos], bk)]
-    t0 = time.perf_counter()
-    init, init_m, roff = initial_rows(w, np.concatenate([wpos, upos]))
-    nw = wpos.size
-    say(f"initial rows of {wpos.size + upos.size} keys regenerated in "
-        f"{time.perf_counter() - t0:.0f}s")
-
-    # ---- slots bit-exact, per table; rowrefs bit-exact (rank) or naming the right key
-    t0 = time.perf_counter()
-    ktab = O.table_of(keys, w.n_tables)
-    slot_o = np.empty(nw, dtype=np.int64)
-    rank_o = np.empty(nw, dtype=np.int64)
-    for t in range(w.n_tables):
-        mt = ktab == t
-        keys_t = keys[mt] if w.n_tables > 1 else keys
-        pos_in_t = (np.cumsum(mt) - 1)[wpos] if w.n_tables > 1 else wpos
-        sel = np.nonzero(ktab[wpos] == t)[0]
-        nh = O.n_home_slots(keys_t.size, w.load_factor)
-        _, sl_t, rk_t = O.slots_of_sample(keys_t, nh, pos_in_t[sel])
-        slot_o[sel] = sl_t
-        rank_o[sel] = rk_t
-    say(f"oracle slots of {want.size} keys in {time.perf_counter() - t0:.0f}s")
-    at = np.searchsorted(want, bkeys[occ])
-    assert np.array_equal(res["slot"][occ], slot_o[at])
-    if simple:
-        assert np.array_equal(res["rowref"][occ].astype(np.int64), rank_o[at])
-        # the unique list holds each sampled touched key's rowref, with its occurrence count
-        pr = rank_o[np.searchsorted(want, pick_keys)]
-        u_at = np.searchsorted(uq, pr)
-        assert np.array_equal(uq[u_at], pr)
-    else:
-        assert np.array_equal(rowref_keys(res["rowref"][occ]).view(np.uint64), bkeys[occ])
-        ukeys = rowref_keys(res["unique"]).view(np.uint64)
-        order = np.argsort(ukeys)
-        u_at = order[np.searchsorted(ukeys[order], pick_keys)]
-        assert np.array_equal(ukeys[u_at], pick_keys)
-    assert np.array_equal(res["count"][u_at], bcount[pick])
-    say(f"{occ.size} slots, {pick.size} unique rows and counts match")
-
-    # ---- pooled output of the sampled samples: the oracle over just their keys
-    fsel = np.searchsorted(want, fwd_keys)
-    ot = O.Table(fwd_keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor, w.acc_init,
-                 P.take(init, roff, fsel), master=P.take(init_m, roff, fsel))
-    say(f"oracle table over {fwd_keys.size} keys of the sampled samples")
-    out_o, miss_o = ot.forward(sub_keys.view(np.int64), sub_off, w.out_dtype)
-    assert miss_o == 0
-    P.check_pooled(res["out"][samp], out_o, P.pooled_scale(ot, sub_keys.view(np.int64), sub_off),
-                   w.out_dtype)
-    say(f"{samp.size} sampled samples ({bag_ids.size} bags) pooled within tolerance")
-    del ot
-
-    # ---- update of the sampled touched keys: the batch restricted to their occurrences (every
-    # bag kept, other keys dropped) gives them the same gradient sums
-    m = np.isin(bkeys, pick_keys)
-    bag_of = np.repeat(np.arange(lens.size, dtype=np.int64), lens)
-    upd_off = np.concatenate([[0], np.cumsum(np.bincount(bag_of[m], minlength=lens.size))])
-    upd_keys = bkeys[m].view(np.int64)
-    del bag_of
-    psel = np.searchsorted(want, pick_keys)
-    ot = O.Table(pick_keys, dims, w.row_dtype, w.has_master, w.n_tables, w.load_factor,
-                 w.acc_init, P.take(init, roff, psel), master=P.take(init_m, roff, psel),
-                 ftrl=ftrl is not None)
-    bud = P.Budget(ot)
-    t0 = time.perf_counter()
-    if ftrl is None:
-        bud.oracle_step(ot, upd_keys, upd_off, bt["grad"], w.lr, w.eps)
-    else:
-        bud.oracle_step_ftrl(ot, upd_keys, upd_off, bt["grad"], *ftrl)
-    say(f"oracle update of {pick.size} rows over {upd_keys.size} occurrences in "
-        f"{time.perf_counter() - t0:.0f}s")
-    rows_g, acc_g, mst_g = export(pick_keys)
-    P.check_state(ot, bud, pick_keys, rows_g, acc_g, mst_g if w.has_master else None,
-                  None if ftrl is None else export_linear(pick_keys))
-    # untouched resident keys: bit-identical to their initial state
-    usel = np.arange(nw, nw + upos.size)
-    ru, au, mu = export(keys[upos])
-    assert np.all(au == np.float32(w.acc_init))
-    assert ru.tobytes() == P.take(init, roff, usel).tobytes()
-    if init_m is not None:
-        assert mu.tobytes() == P.take(init_m, roff, usel).tobytes()
-    if ftrl is not None:
-        assert np.all(export_linear(keys[upos]) == 0)
-    say(f"{pick.size} updated rows within budget; {upos.size} untouched rows bit-identical")
+def test_pass_scale_two_steps():
+    host = host_available()
+    free, _ = torch.cuda.mem_get_info()
+    if host < PASS_HOST_BYTES or free < PASS_DEVICE_BYTES:
+        pytest.skip(f"800M-key table needs ~{PASS_HOST_BYTES >> 30} GiB host memory and "
+                    f"~{PASS_DEVICE_BYTES >> 30} GiB device memory free; have {host >> 30} and "
+                    f"{free >> 30}")
+    w = W.F64_PASS
+    T, keys = build_flash(w)
+    two_steps(w, T, keys)
+    T.close()
