@@ -291,8 +291,15 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   const int f0 = (int)((uint32_t)j0 - div_fields(a.d, (uint32_t)j0) * (uint32_t)F);
 
   uint32_t miss = 0;
-  // scans run, scans past the home bucket, buckets read, most buckets one scan read
-  uint32_t st_scan = 0, st_past = 0, st_read = 0, st_max = 0;
+  // probe statistics go straight to LDS counters (when asked for), holding no registers across
+  // the probe loops: scans run, scans past the home bucket, buckets read, most buckets of a scan
+  const bool stats = a.stats != nullptr;
+  auto count_scan = [&](uint32_t nread) {
+    atomicAdd(&s_stat[0], 1u);
+    atomicAdd(&s_stat[1], nread > 1 ? 1u : 0u);
+    atomicAdd(&s_stat[2], nread);
+    atomicMax(&s_stat[3], nread);
+  };
   if (a.mode == 2) {
     // pool only: the rowrefs of an earlier probe launch
     if (in_lds)
@@ -313,10 +320,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
       uint32_t nread;
       const uint32_t rr = probe_key<VAR>(a.d, key, bf, sl, nread);
       miss += (rr == kMiss);
-      st_scan += nread != 0;
-      st_past += nread > 1;
-      st_read += nread;
-      st_max = max(st_max, nread);
+      if (stats && nread) count_scan(nread);
       if (in_lds) s_rr[i] = rr;
       a.rowref[pos] = rr;
       if (a.slot) a.slot[pos] = sl;
@@ -393,13 +397,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
               if (sub == 0 && i < nk) {
                 const uint32_t rr = key == kEmpty ? kMiss : h.rr;
                 miss += (rr == kMiss);
-                if (key != kEmpty) {
-                  const uint32_t nread = (uint32_t)ext[r] + 1u;
-                  st_scan += 1u;
-                  st_past += nread > 1;
-                  st_read += nread;
-                  st_max = max(st_max, nread);
-                }
+                if (stats && key != kEmpty) count_scan((uint32_t)ext[r] + 1u);
                 if (in_lds) s_rr[i] = rr;
                 a.rowref[base + i] = rr;
                 if (a.slot) {
@@ -421,15 +419,9 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
     }
   }
   if (miss) atomicAdd(&s_miss, miss);
-  if (a.stats && st_scan) {
-    atomicAdd(&s_stat[0], st_scan);
-    atomicAdd(&s_stat[1], st_past);
-    atomicAdd(&s_stat[2], st_read);
-    atomicMax(&s_stat[3], st_max);
-  }
   __syncthreads();
   if (tid == 0 && s_miss && a.n_miss) atomicAdd(a.n_miss, (unsigned long long)s_miss);
-  if (tid == 0 && a.stats && s_stat[0]) {
+  if (tid == 0 && stats && s_stat[0]) {
     atomicAdd(a.stats + 0, (unsigned long long)s_stat[0]);
     atomicAdd(a.stats + 1, (unsigned long long)s_stat[1]);
     atomicAdd(a.stats + 2, (unsigned long long)s_stat[2]);
