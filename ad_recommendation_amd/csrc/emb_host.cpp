@@ -977,8 +977,8 @@ bool validate_on() {
 // never decrease and end at nnz; with rowrefs, each is a miss or names a whole row of its bag's
 // field -- and synchronises the stream to read the verdict.  EMB_EINVAL names what failed.
 int validate_batch(EmbTable* t, const int32_t* d_offsets, int64_t n_bags, int64_t nnz,
-                   const uint32_t* d_rowref, hipStream_t st) {
-  if (!t->d_vflag) {
+                   const uint32_t* d_rowref, hipStream_t st, uint32_t* d_flag = nullptr) {
+  if (!d_flag && !t->d_vflag) {
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&t->d_vflag), 256);
     if (e != hipSuccess) {
       t->d_vflag = nullptr;
@@ -991,10 +991,10 @@ int validate_batch(EmbTable* t, const int32_t* d_offsets, int64_t n_bags, int64_
   v.n_bags = (int32_t)n_bags;
   v.nnz = (int32_t)nnz;
   v.rowref = nnz > 0 ? d_rowref : nullptr;
-  v.flag = t->d_vflag;
+  v.flag = d_flag ? d_flag : t->d_vflag;
   hipError_t e = launch_validate(v, st);
   uint32_t flag = 0;
-  if (e == hipSuccess) e = hipMemcpyAsync(&flag, t->d_vflag, 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(&flag, v.flag, 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "EMB_VALIDATE check");
   if (flag & 1u) return fail(EMB_EINVAL, "EMB_VALIDATE: offsets[0] is not 0");
@@ -1092,7 +1092,8 @@ namespace {
 int sparse_bwd(EmbTable* t, int stage, const uint32_t* d_rowref, const int32_t* d_offsets,
                int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype, float lr,
                float eps, int ftrl, float beta, float l1, float l2, void* d_ws, size_t ws_bytes,
-               uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream) {
+               uint32_t* d_unique, int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream,
+               uint32_t* d_vflag = nullptr) {
   if (!t) return fail(EMB_EINVAL, "null table");
   if (n_bags < 0 || nnz < 0 || n_bags >= (1ll << 31) || nnz >= (1ll << 31))
     return fail(EMB_EINVAL, "n_bags and nnz must be in [0, 2^31)");
@@ -1118,7 +1119,7 @@ int sparse_bwd(EmbTable* t, int stage, const uint32_t* d_rowref, const int32_t* 
     return fail(EMB_ESTATE, "apply without a sparse_bwd_dedup of this workspace and these sizes");
   if (stage != 2 && validate_on() && n_bags > 0) {
     const int rc = validate_batch(t, d_offsets, n_bags, nnz, d_rowref,
-                                  static_cast<hipStream_t>(stream));
+                                  static_cast<hipStream_t>(stream), d_vflag);
     if (rc) return rc;
   }
   // a dedup enables one apply; any other backward call may overwrite its workspace
@@ -1186,6 +1187,27 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
                        int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream) {
   return sparse_bwd(t, 0, d_rowref, d_offsets, n_bags, nnz, d_grad, grad_dtype, lr, eps, 0, 0.f,
                     0.f, 0.f, d_ws, ws_bytes, d_unique, d_count, d_n_unique, stream);
+}
+
+int sparse_adagrad_bwd_noalloc(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                               int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
+                               float lr, float eps, uint32_t* d_unique, int32_t* d_count,
+                               int64_t* d_n_unique, emb_stream_t stream) {
+  if (!t) return fail(EMB_EINVAL, "null table");
+  if (n_bags < 0 || nnz < 0 || nnz >= (1ll << 31)) return fail(EMB_EINVAL, "bad sizes");
+  // the scratch holds the workspace and, at its end, the EMB_VALIDATE flag word
+  const size_t need = plan_bwd(nnz, t->rowref_space, t->max_dim, t->row_dtype == EMB_F16,
+                               t->classed).bytes;
+  const size_t cap = scratch_bytes() - 256;
+  if (need > cap)
+    return fail(EMB_ENOSPACE, "batch needs " + std::to_string(need) + " bytes of backward "
+                              "workspace; the static scratch holds " + std::to_string(cap));
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  uint32_t* vflag = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + cap);
+  return sparse_bwd(t, 0, d_rowref, d_offsets, n_bags, nnz, d_grad, grad_dtype, lr, eps, 0, 0.f,
+                    0.f, 0.f, ws, cap, d_unique, d_count, d_n_unique, stream, vflag);
 }
 
 int sparse_ftrl_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,

@@ -150,6 +150,11 @@ struct ValArgs {
 };
 hipError_t launch_validate(const ValArgs& a, hipStream_t st);
 
+// The library's static backward scratch: its size in bytes, and its device address on the
+// current device (looked up once per device).
+size_t scratch_bytes();
+hipError_t scratch_address(void** ptr);
+
 
 struct BwdLaunch {
   DevDesc d;

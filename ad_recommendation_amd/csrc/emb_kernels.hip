@@ -11,7 +11,9 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "emb_internal.h"
 
@@ -1631,6 +1633,34 @@ hipError_t launch_validate(const ValArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_validate, dim3(1), dim3(kBlock), 0, st, a);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- static backward scratch
+// The backward's workspace for callers that cannot allocate device memory (code under graph
+// capture, allocation-free training loops): one array per device, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not the device array; its device address is
+// looked up once per device with hipGetSymbolAddress and only that address is used.
+constexpr size_t kScratchBytes = 64ull << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+size_t scratch_bytes() { return kScratchBytes; }
+
+hipError_t scratch_address(void** ptr) {
+  static std::mutex mu;
+  static std::vector<void*> per_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev >= per_device.size()) per_device.resize((size_t)dev + 1, nullptr);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 // ================================================================ launchers

@@ -71,6 +71,8 @@ def lib() -> C.CDLL:
         "bwd_workspace_bytes": [_VP, _I64, _I64, C.POINTER(C.c_size_t)],
         "sparse_adagrad_bwd": [_VP, _VP, _VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float, _VP,
                                C.c_size_t, _VP, _VP, _VP, _VP],
+        "sparse_adagrad_bwd_noalloc": [_VP, _VP, _VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float,
+                                       _VP, _VP, _VP, _VP],
         "sparse_ftrl_bwd": [_VP, _VP, _VP, _I64, _I64, _VP, _I32, C.c_float, C.c_float, C.c_float,
                             C.c_float, _VP, C.c_size_t, _VP, _VP, _VP, _VP],
         "lookup_probe": [_VP, _VP, _VP, _I64, _I64, _VP, _VP, _VP, _VP],
@@ -120,7 +122,7 @@ def exported_symbols():
             "sparse_ftrl_apply",
             "table_build_workspace_bytes", "table_create_on_device",
             "table_export", "table_fill_state", "table_key_rowref", "table_rowref_keys",
-            "table_probe_stats", "emb_timing_enable",
+            "table_probe_stats", "sparse_adagrad_bwd_noalloc", "emb_timing_enable",
             "emb_timing_read", "table_destroy", "emb_last_error"]
 
 
@@ -265,6 +267,18 @@ def sparse_adagrad_bwd(h, rowref, offsets, n_bags: int, nnz: int, grad, grad_dty
         _dp(grad, (torch.float32, torch.float16)), int(grad_dtype), float(lr), float(eps),
         _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(), _dp(unique, (torch.int32,)),
         _dp(count, (torch.int32,)), _dp(n_unique, (torch.int64,)), _stream(stream)))
+
+
+def sparse_adagrad_bwd_noalloc(h, rowref, offsets, n_bags: int, nnz: int, grad, grad_dtype: int,
+                               lr: float, eps: float, unique=None, count=None, n_unique=None,
+                               stream=None):
+    """sparse_adagrad_bwd on the library's static scratch: no workspace, no allocation."""
+    import torch
+    _check(lib().sparse_adagrad_bwd_noalloc(
+        h, _dp(rowref, (torch.int32,)), _dp(offsets, (torch.int32,)), int(n_bags), int(nnz),
+        _dp(grad, (torch.float32, torch.float16)), int(grad_dtype), float(lr), float(eps),
+        _dp(unique, (torch.int32,)), _dp(count, (torch.int32,)), _dp(n_unique, (torch.int64,)),
+        _stream(stream)))
 
 
 def sparse_ftrl_bwd(h, rowref, offsets, n_bags: int, nnz: int, grad, grad_dtype: int,

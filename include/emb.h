@@ -238,6 +238,27 @@ int sparse_adagrad_bwd(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_o
                        int32_t* d_count, int64_t* d_n_unique, emb_stream_t stream);
 
 /*
+ * sparse_adagrad_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, allocation-free training loops, harnesses that forbid
+ * hipMalloc).  The workspace is a static device array inside the library, 64 MiB per device,
+ * held by every device the library runs on until the process ends; its address is looked up
+ * once per device.  The call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine, also with EMB_VALIDATE=1 (its flag word lives at the array's end).
+ *   Limit: batches whose bwd_workspace_bytes exceed 64 MiB - 256 bytes get EMB_ENOSPACE before
+ *          any device work (about 3M occurrences of rows up to 64 elements wide).
+ *   Sharing: every call on one device uses that device's one array, and each call leaves its
+ *          contents behind (the call itself needs none of them cleared).  Calls that overlap on
+ *          one device -- on two streams, from two threads, or on two tables -- race; order
+ *          them on one stream or with events.
+ * Arguments, outputs and other errors as for sparse_adagrad_bwd; results are bit-identical to
+ * it for the same inputs.
+ */
+int sparse_adagrad_bwd_noalloc(EmbTable* t, const uint32_t* d_rowref, const int32_t* d_offsets,
+                               int64_t n_bags, int64_t nnz, const void* d_grad, int32_t grad_dtype,
+                               float lr, float eps, uint32_t* d_unique, int32_t* d_count,
+                               int64_t* d_n_unique, emb_stream_t stream);
+
+/*
  * The same backward with the FTRL update in place of Adagrad, on tables created with
  * EMB_FLAG_FTRL (EMB_ESTATE otherwise).  The JD ads article's sparse-optimizer section names FTRL
  * as the Adagrad variant used for sparse features; the update is per-coordinate FTRL-Proximal
