@@ -53,5 +53,35 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "san", "libmi355emb_san.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The host runtime built with AddressSanitizer and UndefinedBehaviorSanitizer (host code only,
+    compiled by g++; the kernels object is the regular build's), linked into SAN_LIB.  The CPU
+    tests load it in a process started with the ASan runtime preloaded.  Returns its path."""
+    k_obj = os.path.join(BUILD, "emb_kernels.o")
+    if not os.path.exists(k_obj):
+        build(verbose)
+    d = os.path.dirname(SAN_LIB)
+    os.makedirs(d, exist_ok=True)
+    h_obj = os.path.join(d, "emb_host_san.o")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer"]
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-Wall", *san, "-I", os.path.join(ROOT, "include"),
+          "-I", CSRC, "-I", os.path.join(rocm, "include"), "-D__HIP_PLATFORM_AMD__", "-c",
+          os.path.join(CSRC, "emb_host.cpp"), "-o", h_obj], verbose)
+    tmp = SAN_LIB + ".tmp"
+    _run(["g++", "-shared", "-fPIC", *san[:1], "-o", tmp, k_obj, h_obj,
+          "-L", os.path.join(rocm, "lib"), "-Wl,-rpath," + os.path.join(rocm, "lib"), "-lamdhip64",
+          "-lpthread"], verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -22,7 +22,9 @@ FLAG_TRACK_TOUCHED = 8  # keep the device bitmap of updated rows for pass_writeb
 FLAG_FTRL = 16          # keep the FTRL linear state for sparse_ftrl_bwd
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmi355emb.so")
+# MI355EMB_LIB selects another build of the same library (the sanitized host build of the CPU
+# tests); the default is the in-tree one
+LIB_PATH = os.environ.get("MI355EMB_LIB") or os.path.join(_HERE, "libmi355emb.so")
 
 _STATUS = {0: "EMB_OK", -1: "EMB_EINVAL", -2: "EMB_EDUPKEY", -3: "EMB_ESENTINEL", -4: "EMB_ERANGE",
            -5: "EMB_ENOSPACE", -6: "EMB_ESTATE", -7: "EMB_EHIP", -8: "EMB_ENOMEM"}

@@ -281,3 +281,26 @@ def test_mixed_width_state_arrays_are_padded_by_a_widest_row():
     F = emb.Table([16] * 4, emb.EMB_F32, False, 1, 0.5, 0.1,
                   (np.arange(1000, dtype=np.uint64) | (np.uint64(1) << np.uint64(48))))
     assert F.info["state_bytes"] < (F.info["total_elems"] * 8) + 1024   # fixed width: no pad
+
+
+def test_bench_algorithmic_bytes_follow_the_byte_model():
+    """B_alg and B_min of one step, on a hand-made batch whose counts are known: 2 fields of width
+    8 (fp16 rows, fp32 master, fp16 output and gradient), 2 samples, 7 occurrences of 3 rows, with
+    one row crossing no piece.  The sort's passes are not part of B_alg."""
+    import bench
+    from dataclasses import replace
+    w = replace(W.scaled(W.F100, n_keys=100, batch=2), n_fields=2, dim=8)
+    st = {"nnz": 7, "U": 3, "bags": 4, "occ_elems": 7 * 8, "bag_elems": 4 * 8,
+          "u_elems_inside": 3 * 8, "u_elems_cross": 0, "u_cross": 0, "n_pieces": 1, "pdim": 8,
+          "classed": False}
+    # forward: per occurrence key 8 + probe 12 + rowref 4 + row 8*2; per bag offset 4 + out 8*2
+    fwd = 7 * (8 + 12 + 4 + 16) + 4 * (4 + 16)
+    # backward: per occurrence rowref 4 + gradient 8*2; per bag offset 4; per row its state
+    # read and written (row 2, acc 4, master 4 bytes per element, twice) plus rowref and count
+    bwd = 7 * (4 + 16) + 4 * 4 + 3 * 8 * (2 * 2 + 8 + 8) + 12 * 3
+    assert bench.b_alg_bytes(st, w) == fwd + bwd
+    # compulsory bytes: each datum once -- one probe hit and one row read per distinct row
+    bmin = 7 * 12 + 3 * 12 + 3 * 8 * 2 + 4 * (4 + 16) + 4 * (4 + 16) + 7 * 4 + 3 * 8 * (2 * 2 + 8 + 8)
+    assert bench.b_min_bytes(st, w) == bmin
+    assert bench.b_alg_bytes(st, w, ftrl=True) == fwd + bwd + 3 * 8 * 8
+    assert "sort_scatter" in bench.SORT_KERNELS and "update_pieces" not in bench.SORT_KERNELS
