@@ -266,7 +266,54 @@ __device__ __forceinline__ typename F32V<16 / sizeof(RowT)>::t pool_rows(const D
   return acc;
 }
 
-template <typename RowT, typename OutT, bool VAR, bool COOP>
+// Probe statistics of one thread: scans run, scans past the home bucket, buckets read, most
+// buckets one scan read.  flush() reduces them over the wave (every lane must call it) and adds
+// them to the block's four LDS counters; the STATS = false form holds and does nothing.
+// (The STATS = false form keeps a runtime-guarded LDS path that never runs, since the launcher
+// sends counting launches to the STATS instantiation: with it the compiler allocates the forward
+// the same 94 registers, five waves per SIMD, as without statistics; an empty form made it 104.)
+template <bool STATS> struct ProbeStats {
+  uint32_t* s;
+  bool on;
+  __device__ __forceinline__ ProbeStats(uint32_t* s_, bool on_) : s(s_), on(on_) {}
+  __device__ __forceinline__ void add(uint32_t nread) {
+    if (on) {
+      atomicAdd(&s[0], 1u);
+      atomicAdd(&s[1], nread > 1 ? 1u : 0u);
+      atomicAdd(&s[2], nread);
+      atomicMax(&s[3], nread);
+    }
+  }
+  __device__ __forceinline__ void flush(uint32_t*) {}
+};
+template <> struct ProbeStats<true> {
+  uint32_t scan = 0, past = 0, read = 0, most = 0;
+  __device__ __forceinline__ ProbeStats(uint32_t*, bool) {}
+  __device__ __forceinline__ void add(uint32_t nread) {
+    scan += 1u;
+    past += nread > 1 ? 1u : 0u;
+    read += nread;
+    most = max(most, nread);
+  }
+  __device__ __forceinline__ void flush(uint32_t* s) {
+    for (int o = 32; o >= 1; o >>= 1) {
+      scan += __shfl_xor(scan, o, 64);
+      past += __shfl_xor(past, o, 64);
+      read += __shfl_xor(read, o, 64);
+      most = max(most, (uint32_t)__shfl_xor(most, o, 64));
+    }
+    if (lane_id() == 0 && scan) {
+      atomicAdd(&s[0], scan);
+      atomicAdd(&s[1], past);
+      atomicAdd(&s[2], read);
+      atomicMax(&s[3], most);
+    }
+  }
+};
+
+// STATS: the instantiation that counts probe statistics (per-thread counters, reduced per wave at
+// the end of the probe); the others carry none of it.
+template <typename RowT, typename OutT, bool VAR, bool COOP, bool STATS>
 __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2) {
   constexpr int EPL = 16 / (int)sizeof(RowT);
   typedef typename F32V<EPL>::t AccV;
@@ -293,15 +340,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   const int f0 = (int)((uint32_t)j0 - div_fields(a.d, (uint32_t)j0) * (uint32_t)F);
 
   uint32_t miss = 0;
-  // probe statistics go straight to LDS counters (when asked for), holding no registers across
-  // the probe loops: scans run, scans past the home bucket, buckets read, most buckets of a scan
-  const bool stats = a.stats != nullptr;
-  auto count_scan = [&](uint32_t nread) {
-    atomicAdd(&s_stat[0], 1u);
-    atomicAdd(&s_stat[1], nread > 1 ? 1u : 0u);
-    atomicAdd(&s_stat[2], nread);
-    atomicMax(&s_stat[3], nread);
-  };
+  ProbeStats<STATS> pst(s_stat, !STATS && a.stats != nullptr);
   if (a.mode == 2) {
     // pool only: the rowrefs of an earlier probe launch
     if (in_lds)
@@ -322,7 +361,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
       uint32_t nread;
       const uint32_t rr = probe_key<VAR>(a.d, key, bf, sl, nread);
       miss += (rr == kMiss);
-      if (stats && nread) count_scan(nread);
+      if (nread) pst.add(nread);
       if (in_lds) s_rr[i] = rr;
       a.rowref[pos] = rr;
       if (a.slot) a.slot[pos] = sl;
@@ -414,7 +453,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
               if (sub == 0 && i < nk) {
                 const uint32_t rr = key == kEmpty ? kMiss : h.rr;
                 miss += (rr == kMiss);
-                if (stats && key != kEmpty) count_scan((uint32_t)ext[r] + 1u);
+                if (key != kEmpty) pst.add((uint32_t)ext[r] + 1u);
                 if (in_lds) s_rr[i] = rr;
                 a.rowref[base + i] = rr;
                 if (a.slot) {
@@ -436,9 +475,10 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
     }
   }
   if (miss) atomicAdd(&s_miss, miss);
+  pst.flush(s_stat);
   __syncthreads();
   if (tid == 0 && s_miss && a.n_miss) atomicAdd(a.n_miss, (unsigned long long)s_miss);
-  if (tid == 0 && stats && s_stat[0]) {
+  if (tid == 0 && a.stats && s_stat[0]) {
     atomicAdd(a.stats + 0, (unsigned long long)s_stat[0]);
     atomicAdd(a.stats + 1, (unsigned long long)s_stat[1]);
     atomicAdd(a.stats + 2, (unsigned long long)s_stat[2]);
@@ -1703,7 +1743,11 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
       ((uint64_t)a.d.tab[0].n_buckets + (a.d.n_tables == 2 ? (uint64_t)a.d.tab[1].n_buckets : 0u)) *
       kWordsPerBucket * 8u;
   const bool coop = a.mode != 2 && (a.probe == 1 || (a.probe == 0 && bucket_bytes >= kCoopProbeBytes));
-#define EMB_FWD2(R, O, V, C) EMB_LAUNCH(tm, (k_lookup_pool<R, O, V, C>), grid, blk, 0, ctx.stream, a, gs)
+#define EMB_FWD2(R, O, V, C)                                                                      \
+  do {                                                                                            \
+    if (a.stats) EMB_LAUNCH(tm, (k_lookup_pool<R, O, V, C, true>), grid, blk, 0, ctx.stream, a, gs); \
+    else EMB_LAUNCH(tm, (k_lookup_pool<R, O, V, C, false>), grid, blk, 0, ctx.stream, a, gs);        \
+  } while (0)
 #define EMB_FWD(R, O, V) do { if (coop) EMB_FWD2(R, O, V, true); else EMB_FWD2(R, O, V, false); } while (0)
   if (a.d.row_f16) {
     if (a.out_f16) { if (a.d.var_dim) EMB_FWD(_Float16, _Float16, true); else EMB_FWD(_Float16, _Float16, false); }
