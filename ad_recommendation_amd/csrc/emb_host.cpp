@@ -213,6 +213,7 @@ struct EmbTable {
   size_t arena_bytes = 0;
   int32_t ftrl = 0;  // the table keeps the FTRL linear state z
   size_t off_touched = 0, touched_words = 0;  // bitmap of rowref units updated since the flash
+  size_t off_pstat = 0;  // partial probe statistics (kStatSlots x 4 words, zero in the image)
   std::vector<uint64_t> dirty;  // host: units written back by pass_writeback_touched since cleared
   uint8_t* image = nullptr;
   bool pinned = false;
@@ -275,6 +276,7 @@ struct EmbTable {
     d.cls_shift = cls_shift;
     d.touched = (flags & EMB_FLAG_TRACK_TOUCHED)
                     ? reinterpret_cast<uint32_t*>(d_arena + off_touched) : nullptr;
+    d.pstat = reinterpret_cast<unsigned long long*>(d_arena + off_pstat);
     d.rowref_space = rowref_space;
     // division by the field count as a multiply and shift (exact for dividends below 2^31)
     int l = 0;
@@ -771,7 +773,8 @@ int create_impl(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys, c
   // must stay inside the arena even for an empty table
   T->off_touched = align256(T->off_meta + 4 * 4 * (size_t)T->F);
   T->touched_words = (T->flags & EMB_FLAG_TRACK_TOUCHED) ? ((size_t)T->rowref_space + 31) / 32 : 0;
-  T->arena_bytes = align256(T->off_touched + 4 * T->touched_words) + 4096;
+  T->off_pstat = align256(T->off_touched + 4 * T->touched_words);
+  T->arena_bytes = align256(T->off_pstat + 32 * (size_t)kStatSlots) + 4096;
   if (T->flags & EMB_FLAG_PINNED_STAGING) {
     hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&T->image), T->arena_bytes, 0);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc of the host image");

@@ -17,6 +17,9 @@ constexpr uint32_t kMiss = 0xFFFFFFFFu;
 constexpr uint64_t kMix = 0x9E3779B97F4A7C15ull;  // floor(2^64 / golden ratio)
 constexpr int kMaxFields = 65535;
 constexpr int kMaxDim = 256;
+// Probe statistics are added per block into one of kStatSlots partial slots in the arena (so that
+// the blocks of a launch do not all contend for one counter) and summed by a one-block kernel.
+constexpr int kStatSlots = 4096;
 
 // 64-bit key mix used to place keys; every step is invertible.
 __host__ __device__ inline uint64_t mix64(uint64_t x) {
@@ -64,6 +67,7 @@ struct DevDesc {
   int32_t cls_shift;     // bits of the rowref part of a sort key
   const int32_t* fgsl;   // [F] class (log2 lanes per row) of each field
   uint32_t* touched;     // null, or one bit per rowref unit set when the row is updated
+  unsigned long long* pstat;  // [kStatSlots][4] partial probe statistics, zero between launches
 };
 
 // End-of-PASS write-back of the rows touched since the last flash: the bitmap is read in blocks

@@ -479,10 +479,11 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   __syncthreads();
   if (tid == 0 && s_miss && a.n_miss) atomicAdd(a.n_miss, (unsigned long long)s_miss);
   if (tid == 0 && a.stats && s_stat[0]) {
-    atomicAdd(a.stats + 0, (unsigned long long)s_stat[0]);
-    atomicAdd(a.stats + 1, (unsigned long long)s_stat[1]);
-    atomicAdd(a.stats + 2, (unsigned long long)s_stat[2]);
-    atomicMax(a.stats + 3, (unsigned long long)s_stat[3]);
+    unsigned long long* ps = a.d.pstat + (size_t)(blockIdx.x % (unsigned)kStatSlots) * 4u;
+    atomicAdd(ps + 0, (unsigned long long)s_stat[0]);
+    atomicAdd(ps + 1, (unsigned long long)s_stat[1]);
+    atomicAdd(ps + 2, (unsigned long long)s_stat[2]);
+    atomicMax(ps + 3, (unsigned long long)s_stat[3]);
   }
   if (a.mode == 1) return;  // probe only
 
@@ -1654,6 +1655,43 @@ __global__ __launch_bounds__(kBlock) void k_wb_gather(WbLaunch a) {
     if (w0 + q < a.n_words && bits[q]) a.touched[w0 + q] = 0u;
 }
 
+// ---------------------------------------------------------------- probe statistics
+// Sums the forward's partial probe statistics into the caller's counters and clears the slots
+// for the next counting launch.  One block.
+__global__ __launch_bounds__(kBlock) void k_stats_finish(unsigned long long* pstat,
+                                                         unsigned long long* out) {
+  __shared__ unsigned long long s[4][kBlock];
+  unsigned long long v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+  for (int i = threadIdx.x; i < kStatSlots; i += kBlock) {
+    unsigned long long* p = pstat + 4 * (size_t)i;
+    v0 += p[0];
+    v1 += p[1];
+    v2 += p[2];
+    v3 = p[3] > v3 ? p[3] : v3;
+    p[0] = 0;
+    p[1] = 0;
+    p[2] = 0;
+    p[3] = 0;
+  }
+  s[0][threadIdx.x] = v0;
+  s[1][threadIdx.x] = v1;
+  s[2][threadIdx.x] = v2;
+  s[3][threadIdx.x] = v3;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int t = 1; t < kBlock; ++t) {
+      v0 += s[0][t];
+      v1 += s[1][t];
+      v2 += s[2][t];
+      v3 = s[3][t] > v3 ? s[3][t] : v3;
+    }
+    atomicAdd(out + 0, v0);
+    atomicAdd(out + 1, v1);
+    atomicAdd(out + 2, v2);
+    atomicMax(out + 3, v3);
+  }
+}
+
 // ---------------------------------------------------------------- batch validation
 // One thread per bag: its offsets must not decrease, the first must be 0 and the last nnz; with
 // rowrefs, every occurrence of a well-formed bag must be a miss or start a whole row of the bag's
@@ -1758,6 +1796,10 @@ hipError_t launch_lookup_pool(const FwdLaunch& a, LaunchCtx& ctx) {
   }
 #undef EMB_FWD
 #undef EMB_FWD2
+  if (a.stats) {
+    KTimer ts(ctx, "probe_stats");
+    EMB_LAUNCH(ts, k_stats_finish, dim3(1), blk, 0, ctx.stream, a.d.pstat, a.stats);
+  }
   return hipGetLastError();
 }
 
