@@ -628,7 +628,10 @@ def main():
                     for i in range(args.steps))
     dom_bytes *= per_step_launches
     achieved = dom_bytes / (dom[1] / 1e3) / 1e9
-    traffic = load_traffic(w.name, dominant)
+    # counter traffic was measured on the fused Adagrad step without tracking: other forms run
+    # other kernel instantiations
+    profiled = not (ftrl or args.lifecycle or args.split) and not args.keys
+    traffic = load_traffic(w.name, dominant) if profiled else None
 
     writeback = None
     if args.lifecycle:
@@ -664,7 +667,8 @@ def main():
             sub_rate = (c["nnz"] + c["U"]) / c["median_s"]
             full_s = c["median_s"] * c["full_nnz"] / c["nnz"]
             cpu = {"value": sub_rate, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                   "sample": f"every {c['sub']}th sample of batch 0 of {w.name} ({c['samples']} "
+                   "sample": f"{'every sample' if c['sub'] == 1 else 'every %dth sample' % c['sub']} "
+                             f"of batch 0 of {w.name} ({c['samples']} "
                              f"samples x {w.n_fields} fields: {c['nnz']} lookups, {c['U']} row "
                              f"updates); oracle table built over just those keys (build "
                              f"{c['build_seconds']:.1f}s excluded); forward+backward median of "
