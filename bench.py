@@ -632,6 +632,12 @@ def main():
     # other kernel instantiations
     profiled = not (ftrl or args.lifecycle or args.split) and not args.keys
     traffic = load_traffic(w.name, dominant) if profiled else None
+    # the whole step's counter traffic, when every kernel of the step has been measured
+    counter_step = None
+    if profiled:
+        per = {k: load_traffic(w.name, k) for k in kernels}
+        if all(v is not None for v in per.values()):
+            counter_step = sum(per[k] * kernels[k]["launches_per_step"] for k in kernels)
 
     writeback = None
     if args.lifecycle:
@@ -707,6 +713,13 @@ def main():
                      "frac": alg_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS,
                      "sort_bytes_per_step": sort_step,
                      "amplification_sort": (alg_step + sort_step) / alg_step,
+                     "counter_bytes_per_step": counter_step,
+                     "counter_GB_per_s": (counter_step / (ms / args.steps) / 1e6
+                                          if counter_step else None),
+                     "counter_frac": (counter_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS
+                                      if counter_step else None),
+                     "amplification_counters_vs_b_min": (counter_step / bmin_step
+                                                         if counter_step else None),
                      "b_min_per_step": bmin_step,
                      "sol_frac": bmin_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS,
                      "ms_fwd": ms_fwd, "ms_bwd": ms_bwd},
