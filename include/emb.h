@@ -195,6 +195,9 @@ int lookup_pool_fwd(EmbTable* t, const int64_t* d_keys, const int32_t* d_offsets
  *                 slot h lies in bucket h / 15 and a scan stops at the key or at an empty slot),
  *   d_stats[2] += buckets read by all scans,
  *   d_stats[3]  = max(d_stats[3], the most buckets one scan read).
+ * A scan's buckets are those from its home bucket to the one where it stops; the wave-cooperative
+ * probe also loads the following bucket early for keys homed near their bucket's end, and such a
+ * load is not counted when the home bucket ends the scan.
  * The caller zeroes the counters and reads them when it likes; d_stats = NULL stops the counting.
  * Host only (no device work); d_stats must be 8-byte aligned (EMB_EINVAL).
  */
