@@ -45,6 +45,10 @@ def gpu_stats(T, w, keys, offsets):
     return [s[0] // 2, s[1] // 2, s[2] // 2, s[3]], s
 
 
+def _dev(a, dt=None):
+    return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to("cuda")
+
+
 WORKLOADS = [W.TINY, W.scaled(W.F26, n_keys=500_000, batch=1024),
              W.scaled(W.F40_VARDIM, n_keys=400_000, batch=512),
              W.scaled(W.F64_PASS, n_keys=600_000, batch=256),
@@ -71,7 +75,11 @@ def test_probe_stats_match_oracle(w, flags):
 
 def test_probe_stats_dense_table_reads_many_buckets():
     # load factor 1.0: long clusters, so scans leave their home bucket often and the maximum is
-    # large; both forms agree with the oracle
+    # large, and many keys of a 64-key chunk sit in their bucket's last slots (the cooperative
+    # form's early next-bucket loads, over their per-chunk cap, and scans that outrun them).  Both
+    # forms agree with the oracle on the statistics, and on every occurrence's slot and rowref:
+    # with one table and one row unit per key, a hit's rowref is the rank of its slot among the
+    # table's occupied slots.
     from dataclasses import replace
     w = replace(W.scaled(W.F26, n_keys=300_000, batch=512, name_suffix="_lf1"), load_factor=1.0)
     keys = synth.resident_keys(w)
@@ -79,20 +87,41 @@ def test_probe_stats_dense_table_reads_many_buckets():
     dims = synth.field_dims(w)
     ot = P.oracle_table(w, keys, rows, master, dims)
     bt = synth.batch(w, 0)
-    want = oracle_stats(ot, bt["keys"], bt["offsets"])
+    kk, off = bt["keys"], bt["offsets"]
+    want = oracle_stats(ot, kk, off)
     assert want[1] > want[0] // 10 and want[3] >= 3
+    assert ot.n_tables == 1 and np.all(ot.width == ot.width[0])
+    rank = np.empty(ot.slot.size, dtype=np.int64)
+    rank[np.argsort(ot.slot)] = np.arange(ot.slot.size)
+    kidx, _, slot = ot.lookup(kk, off)
+    hit = kidx >= 0
+    assert hit.mean() > 0.9
+    # keys homed in the last three slots of a bucket, per 64-key chunk of the batch (the chunks
+    # of a block start at its first key, so this is a close stand-in): some chunks hold more
+    # than the 16 that load their next bucket early
+    home = ot.home[np.maximum(kidx, 0)]
+    late = hit & (home % 15 >= 12)
+    n = late.size // 64 * 64
+    assert late[:n].reshape(-1, 64).sum(1).max() > 16
     for flags in (emb.FLAG_PROBE_LANE, emb.FLAG_PROBE_COOP):
         T = gpu_table(w, keys, rows, master, dims, flags)
-        got, _ = gpu_stats(T, w, bt["keys"], bt["offsets"])
+        got, _ = gpu_stats(T, w, kk, off)
         assert got == want
+        k, o = _dev(kk), _dev(off, np.int32)
+        n_bags, nnz = off.size - 1, kk.size
+        out = torch.empty((w.batch, int(dims.sum())), dtype=torch.float32, device="cuda")
+        rr = torch.empty(nnz, dtype=torch.int32, device="cuda")
+        sl = torch.empty(nnz, dtype=torch.int64, device="cuda")
+        emb.lookup_pool_fwd(T.h, k, o, n_bags, nnz, out, emb.EMB_F32, rr, sl)
+        torch.cuda.synchronize()
+        got_rr = rr.cpu().numpy().view(np.uint32).astype(np.int64)
+        assert np.array_equal(sl.cpu().numpy(), slot)
+        assert np.array_equal(got_rr[hit], rank[kidx[hit]])
+        assert np.all(got_rr[~hit] == emb.ROWREF_MISS)
         T.close()
 
 
 # ------------------------------------------------------------------ EMB_VALIDATE
-def _dev(a, dt=None):
-    return torch.from_numpy(np.ascontiguousarray(a if dt is None else a.astype(dt))).to("cuda")
-
-
 def test_validate_accepts_good_batches_and_refuses_bad_offsets(monkeypatch):
     w = W.scaled(W.F26, n_keys=100_000, batch=64)
     keys = synth.resident_keys(w)
