@@ -520,8 +520,16 @@ def main():
                                          w.eps, ws, n_unique=n_unique[i % R:i % R + 1],
                                          stream=main_stream)
             return
+        fwd(i)
+        bwd(i)
+
+    def fwd(i):
+        r = ring[i % R]
         emb.lookup_pool_fwd(T.h, r["keys"], r["offsets"], r["n_bags"], r["nnz"], out,
                             out_code, rowref)
+
+    def bwd(i):
+        r = ring[i % R]
         if ftrl:
             emb.sparse_ftrl_bwd(T.h, rowref, r["offsets"], r["n_bags"], r["nnz"], r["grad"],
                                 g_code, w.lr, FTRL_BETA, FTRL_L1, FTRL_L2, ws,
@@ -590,6 +598,28 @@ def main():
                    "max_displacement_slots": T.info["max_displacement"]}
     log(f"[bench] probe: {probe_stats['frac_past_home_bucket']:.4f} of scans read past the home "
         f"bucket, {probe_stats['buckets_per_scan']:.4f} buckets per scan, at most {ps[3]}")
+
+    # per-step times over one pass of the ring, outside the timed region: events on the step's
+    # stream around each step and, for the fused calls, between its forward and its backward
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(R)]
+    for i in range(R):
+        evs[i][0].record()
+        if args.split:
+            step(i)
+        else:
+            fwd(i)
+            evs[i][1].record()
+            bwd(i)
+        evs[i][2].record()
+    torch.cuda.synchronize()
+    calib_steps += R
+    per_step_ms = {"t_step": [e[0].elapsed_time(e[2]) for e in evs]}
+    if not args.split:
+        per_step_ms["t_fwd"] = [e[0].elapsed_time(e[1]) for e in evs]
+        per_step_ms["t_bwd"] = [e[1].elapsed_time(e[2]) for e in evs]
+    medians = {k + "_median_ms": float(np.median(v)) for k, v in per_step_ms.items()}
+    log("[bench] per-step medians over the ring (ms): " +
+        ", ".join(f"{k} {v:.4f}" for k, v in medians.items()))
 
     cold = None
     if args.flush_mall:
@@ -722,7 +752,7 @@ def main():
                                                          if counter_step else None),
                      "b_min_per_step": bmin_step,
                      "sol_frac": bmin_step / (ms / args.steps) / 1e6 / HBM_PEAK_GBS,
-                     "ms_fwd": ms_fwd, "ms_bwd": ms_bwd},
+                     "ms_fwd": ms_fwd, "ms_bwd": ms_bwd, **medians},
         "kernels": kernels,
     }
     print(json.dumps(res), flush=True)

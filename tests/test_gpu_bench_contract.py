@@ -40,6 +40,10 @@ def test_bench_prints_one_consistent_json_line():
     assert s["b_min_per_step"] < s["alg_bytes_per_step"]
     assert s["amplification_sort"] == pytest.approx(
         (s["alg_bytes_per_step"] + s["sort_bytes_per_step"]) / s["alg_bytes_per_step"])
+    # medians of the per-step event times over one pass of the ring
+    m = {k: s[k] for k in ("t_step_median_ms", "t_fwd_median_ms", "t_bwd_median_ms")}
+    assert all(v > 0 for v in m.values())
+    assert m["t_fwd_median_ms"] < m["t_step_median_ms"] and m["t_bwd_median_ms"] < m["t_step_median_ms"]
     p = d["probe_stats"]
     assert p["scans"] > 0 and 1.0 <= p["buckets_per_scan"] <= p["max_buckets_one_scan"]
     assert d["pass_flash"]["bytes"] > 0
