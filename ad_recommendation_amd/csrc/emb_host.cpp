@@ -524,6 +524,7 @@ int device_layout(EmbTable* T, const uint64_t* K, size_t N, const DevBuild& db,
     if (s.n_buckets > 0xFFFFFFF0ull) return fail(EMB_ERANGE, "table too large");
     s.bucket_base = bb;
     bb += s.n_buckets;
+    if (bb > 0xFFFFFFFFull) return fail(EMB_ERANGE, "bucket arrays exceed 2^32 buckets");
     s.rowref_base = (uint32_t)rr;
     rr += tot_u;
     if (rr >= 0xFFFFFFFFull) return fail(EMB_ERANGE, "rowref space exceeds 32 bits");
@@ -727,6 +728,7 @@ int create_impl(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys, c
     if (s.n_buckets > 0xFFFFFFF0ull) return fail(EMB_ERANGE, "table too large");
     s.bucket_base = T->total_buckets;
     T->total_buckets += s.n_buckets;
+    if (T->total_buckets > 0xFFFFFFFFull) return fail(EMB_ERANGE, "bucket arrays exceed 2^32 buckets");
     s.rowref_base = (uint32_t)rr_total;
     for (const Entry& en : E) rr_total += (uint64_t)T->gran[(int)(en.key >> 48)];
     if (rr_total >= 0xFFFFFFFFull) return fail(EMB_ERANGE, "rowref space exceeds 32 bits");

@@ -73,6 +73,11 @@ __device__ __forceinline__ typename F32V<N>::t to_f32(typename VecOf<T, N>::t v)
 
 // ---------------------------------------------------------------- wave / block helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+// Set bits of a wave-wide mask in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 #pragma unroll
@@ -103,16 +108,51 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wsum
 }
 
 // ---------------------------------------------------------------- probe
+// Both tables' descriptors as table 0's values plus table 1's differences from them.  Both
+// tables' buckets lie in one array, so a bucket is also named by its index from table 0's first
+// bucket.  Picking a table per lane as a select between the two tables' fields in the kernel
+// argument lets the compiler turn the select into a per-lane load from the argument block, a
+// memory round trip in front of every bucket read; selecting a difference or zero keeps it a
+// register operation, and bucket addresses keep the global address space of table 0's pointer.
+struct Tabs {
+  const uint64_t* base;     // table 0's first bucket
+  uint32_t dbk;             // table 1's first bucket minus table 0's, in buckets (mod 2^32)
+  uint32_t nh0, dnh;        // home slots: table 0's, table 1's minus table 0's
+  uint32_t nbk0, dnbk;      // buckets: likewise
+  bool two;
+  // bucket index from table 0's first bucket of bucket b of table t
+  __device__ __forceinline__ uint32_t global_bucket(uint32_t t, uint32_t b) const {
+    return b + (t ? dbk : 0u);
+  }
+  __device__ __forceinline__ const uint64_t* bucket(uint32_t gb) const {
+    return base + (uint64_t)gb * kWordsPerBucket;
+  }
+};
+__device__ __forceinline__ Tabs scalar_tabs(const DevDesc& d) {
+  Tabs t;
+  t.two = d.n_tables == 2;
+  t.base = d.tab[0].buckets;
+  t.nh0 = d.tab[0].n_home;
+  t.nbk0 = d.tab[0].n_buckets;
+  t.dbk = t.two ? (uint32_t)((d.tab[1].buckets - d.tab[0].buckets) / kWordsPerBucket) : 0u;
+  t.dnh = t.two ? d.tab[1].n_home - t.nh0 : 0u;
+  t.dnbk = t.two ? d.tab[1].n_buckets - t.nbk0 : 0u;
+  return t;
+}
+// The table of a key: (key & 1) when the table is split in two, else 0.
+__device__ __forceinline__ uint32_t table_of_key(const Tabs& tb, uint64_t key) {
+  return (tb.two && (key & 1ull)) ? 1u : 0u;
+}
 struct TabSel {
   const uint64_t* buckets;
   uint32_t n_home, n_buckets;
 };
-__device__ __forceinline__ TabSel pick_tab(const DevDesc& d, uint64_t key) {
-  const bool one = (d.n_tables == 2) && (key & 1ull);
+__device__ __forceinline__ TabSel pick_tab(const Tabs& tb, uint64_t key) {
+  const uint32_t t = table_of_key(tb, key);
   TabSel s;
-  s.buckets = one ? d.tab[1].buckets : d.tab[0].buckets;
-  s.n_home = one ? d.tab[1].n_home : d.tab[0].n_home;
-  s.n_buckets = one ? d.tab[1].n_buckets : d.tab[0].n_buckets;
+  s.buckets = tb.bucket(tb.global_bucket(t, 0u));
+  s.n_home = tb.nh0 + (t ? tb.dnh : 0u);
+  s.n_buckets = tb.nbk0 + (t ? tb.dnbk : 0u);
   return s;
 }
 
@@ -130,12 +170,12 @@ __device__ __forceinline__ uint32_t div_fields(const DevDesc& d, uint32_t n) {
 // `nread` receives the buckets the scan read (0 when no scan runs: the EMPTY key, or a key of
 // another field than its bag's).
 template <bool VAR>
-__device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, int bag_field,
-                                              int64_t& slot, uint32_t& nread) {
+__device__ __forceinline__ uint32_t probe_key(const DevDesc& d, const Tabs& tabs, uint64_t key,
+                                              int bag_field, int64_t& slot, uint32_t& nread) {
   slot = -1;
   nread = 0;
   if (key == kEmpty || (int)(key >> 48) != bag_field) return kMiss;
-  const TabSel tb = pick_tab(d, key);
+  const TabSel tb = pick_tab(tabs, key);
   const uint32_t home = home_slot(mix64(key), tb.n_home);
   uint32_t b = home / (uint32_t)kKeysPerBucket;
   uint32_t l0 = home - b * (uint32_t)kKeysPerBucket;
@@ -181,14 +221,16 @@ __device__ __forceinline__ uint32_t probe_key(const DevDesc& d, uint64_t key, in
 
 // In the wave-cooperative form, the eight lanes of a lane group read one bucket together, lane s
 // loading 16 bytes (slots 2s and 2s+1; lane 7's second word is the prefix), so one load
-// instruction touches eight buckets instead of 64.  It costs more instructions per key, but when
-// the buckets span more memory than the translation caches reach, each of the per-lane form's
-// eight instructions re-misses on 64 pages.  Measured on MI355X: random 128-byte lines read by
-// one lane each come at ~10 G lines/s against ~48 G lines/s read by eight lanes each.  On the
-// 64-field, batch-131072 forward the cooperative form takes 2.7-2.9 ms at 200M, 400M and 800M
-// keys (3.4, 6.8 and 13.6 GB of buckets) where the per-lane form takes 3.4, 5.2 and 5.8 ms; the
-// per-lane form takes 2.0 ms at 100M keys (1.7 GB), and on a 50M-key table with 0.7 GB of buckets
-// it is the faster one (1.35 against 2.18 ms on the 100-field forward).  Hence the 2 GiB switch.
+// instruction touches eight buckets instead of 64.  When the buckets span more memory than the
+// translation caches reach, each of the per-lane form's eight instructions re-misses on 64 pages.
+// Measured on MI355X: random 128-byte lines read by one lane each come at ~10 G lines/s against
+// ~48 G lines/s read by eight lanes each.  On the 64-field, batch-131072 forward the per-lane form
+// takes 3.4, 5.2 and 5.8 ms at 200M, 400M and 800M keys (3.4, 6.8 and 13.6 GB of buckets); the
+// cooperative form took 2.7-2.9 ms there in its first version and takes 1.70 ms at 800M keys now
+// (early next-bucket loads, each key evaluated once from ballots, table descriptors in scalar
+// registers).  Below 2 GiB of buckets the per-lane form is as fast or faster: 1.31 against 1.34 ms
+// on the 100-field forward (0.7 GB of buckets), 0.282 against 0.435 ms on the mixed-width 40-field
+// one, whose cooperative form keeps the group evaluation.  Hence the 2 GiB switch.
 struct BucketHit {
   bool stop;      // the key or an empty slot was found in this bucket
   uint32_t rr;    // rowref on a hit, kMiss otherwise
@@ -232,6 +274,32 @@ __device__ __forceinline__ BucketHit eval_bucket(const DevDesc& d, u64x2 v, uint
   }
   h.rr = hit ? prefix + units : kMiss;
   return h;
+}
+
+// Lanes whose second loaded word is a slot (in each group of eight, lane 7's is the prefix word).
+constexpr uint64_t kSlotLanes = 0x7F7F7F7F7F7F7F7Full;
+
+// One key's scan through one bucket from the bucket's per-slot bits, split by slot parity: bit s of
+// mx / ox is slot 2s (s < 8), bit s of my / oy slot 2s + 1 (s < 7); m: holds the key, o: occupied.
+// l is the first slot at or after l0 that holds the key or is empty (kKeysPerBucket if none), hit
+// whether it holds the key, below the occupied slots before it.
+struct BitScan {
+  int l;
+  bool hit;
+  uint32_t below;
+};
+__device__ __forceinline__ BitScan scan_bits(uint32_t mx, uint32_t my, uint32_t ox, uint32_t oy,
+                                             int l0) {
+  const uint32_t se = (mx | ~ox) & (0xFFu << ((l0 + 1) >> 1)) & 0xFFu;
+  const uint32_t so = (my | ~oy) & (0x7Fu << (l0 >> 1)) & 0x7Fu;
+  const int le = se ? 2 * __builtin_ctz(se) : kKeysPerBucket;
+  const int lo = so ? 2 * __builtin_ctz(so) + 1 : kKeysPerBucket;
+  BitScan r;
+  r.l = min(le, lo);
+  r.hit = r.l < kKeysPerBucket && ((((r.l & 1) ? my : mx) >> (r.l >> 1)) & 1u);
+  r.below = __builtin_popcount(ox & ((1u << ((r.l + 1) >> 1)) - 1u)) +
+            __builtin_popcount(oy & ((1u << (r.l >> 1)) - 1u));
+  return r;
 }
 
 // ---------------------------------------------------------------- forward: probe + sum pool
@@ -327,11 +395,13 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   __shared__ int32_t s_lane0[kFwdBags + 1];       // mixed widths: first packed lane of each bag
   __shared__ uint32_t s_rr[kFwdKeyCap];
   __shared__ uint64_t s_pk[kWaves][64];          // keys of the wave's chunk (EMPTY: no probe)
-  __shared__ uint32_t s_pb[kWaves][64];          // their home buckets
+  __shared__ uint32_t s_pb[kWaves][64];          // their home buckets (index from table 0's first)
   __shared__ uint32_t s_pl[kWaves][64];          // home lane, table, buckets after the home one
   __shared__ int32_t s_sj[kWaves][kSpecKeys];     // chunk keys that read the next bucket early
   __shared__ int32_t s_need[kWaves][64];          // next bucket (after home) a key must read; 0: done
   __shared__ int32_t s_list[kWaves][64];          // chunk keys still unresolved, in lane order
+  __shared__ uint32_t s_pref[kWaves][2][64];      // rowref prefixes of each key's home / next bucket
+  __shared__ uint4 s_tab[2];                      // per table: home slots, buckets, first bucket
   __shared__ uint32_t s_miss;
   __shared__ uint32_t s_stat[4];                  // probe statistics of the block
   const int tid = threadIdx.x;
@@ -341,6 +411,11 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
   for (int i = tid; i <= nb; i += kBlock) s_off[i] = min(max(a.offsets[j0 + i], 0), a.nnz);
   if (tid == 0) s_miss = 0;
   if (tid < 4) s_stat[tid] = 0;
+  if (COOP && tid < 2) {
+    const uint32_t t = a.d.n_tables == 2 ? (uint32_t)tid : 0u;
+    s_tab[tid] = make_uint4(a.d.tab[t].n_home, a.d.tab[t].n_buckets,
+                            (uint32_t)((a.d.tab[t].buckets - a.d.tab[0].buckets) / kWordsPerBucket), 0u);
+  }
   __syncthreads();
   const int32_t base = s_off[0];
   const int32_t nk = max(s_off[nb] - base, 0);
@@ -350,6 +425,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
 
   uint32_t miss = 0;
   ProbeStats<STATS> pst(s_stat, !STATS && a.stats != nullptr);
+  const Tabs tabs = scalar_tabs(a.d);
   if (a.mode == 2) {
     // pool only: the rowrefs of an earlier probe launch
     if (in_lds)
@@ -368,7 +444,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
       bf = bf >= F ? bf - (int)div_fields(a.d, (uint32_t)bf) * F : bf;
       int64_t sl;
       uint32_t nread;
-      const uint32_t rr = probe_key<VAR>(a.d, key, bf, sl, nread);
+      const uint32_t rr = probe_key<VAR>(a.d, tabs, key, bf, sl, nread);
       miss += (rr == kMiss);
       if (nread) pst.add(nread);
       if (in_lds) s_rr[i] = rr;
@@ -379,12 +455,12 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
     // phase 1, wave-cooperative form: each wave probes chunks of 64 keys, eight buckets per load
     // instruction
     const int w = tid >> 6, lane = lane_id(), grp = lane >> 3, sub = lane & 7;
-    const uint64_t lt = (1ull << lane) - 1ull;
     // this lane's key of the wave's next chunk, loaded one chunk ahead
     uint64_t knext = (w * 64 + lane < nk) ? (uint64_t)a.keys[base + w * 64 + lane] : kEmpty;
     for (int c0 = w * 64; c0 < nk; c0 += kBlock) {
       // one lane per key: its field check, hash and home bucket, staged for the lane groups
       int nspec;
+      uint64_t sm;  // keys that load their next bucket early
       {
         const int i = c0 + lane;
         uint64_t key = kEmpty;  // no probe: past the block's keys, or a miss by construction
@@ -401,14 +477,14 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
           bf = bf >= F ? bf - (int)div_fields(a.d, (uint32_t)bf) * F : bf;
           if ((int)(key >> 48) != bf) key = kEmpty;  // a key outside its bag's field misses
         }
-        const TabSel tb = pick_tab(a.d, key);
-        const uint32_t home = key == kEmpty ? 0u : home_slot(mix64(key), tb.n_home);
+        const uint32_t t = table_of_key(tabs, key);
+        const uint4 tb = s_tab[t];  // home slots, buckets, first bucket of the key's table
+        const uint32_t home = key == kEmpty ? 0u : home_slot(mix64(key), tb.x);
         const uint32_t b = home / (uint32_t)kKeysPerBucket;
         const uint32_t l0 = home - b * (uint32_t)kKeysPerBucket;
-        const uint32_t t = (a.d.n_tables == 2 && (key & 1ull)) ? 1u : 0u;
-        const uint32_t follow = min(tb.n_buckets - 1u - b, 0xFFFFFFu);
+        const uint32_t follow = min(tb.y - 1u - b, 0xFFFFFFu);
         s_pk[w][lane] = key;
-        s_pb[w][lane] = b;
+        s_pb[w][lane] = b + tb.z;
         // bits 0-2 and 7: home lane in the bucket; bit 3: table; bits 8-31: buckets that may
         // follow the home bucket (capped; far more than any probe sequence reaches)
         s_pl[w][lane] = (l0 & 7u) | ((l0 & 8u) << 4) | (t << 3) | (follow << 8);
@@ -416,8 +492,8 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
         // first pass, the first kSpecKeys of them in lane order
         const bool spec = key != kEmpty && follow > 0u &&
                           l0 >= (uint32_t)(kKeysPerBucket - kSpecLanes);
-        const uint64_t sm = __ballot(spec);
-        const int si = __popcll(sm & lt);
+        sm = __ballot(spec);
+        const int si = lanes_below(sm);
         if (spec && si < kSpecKeys) s_sj[w][si] = lane;
         nspec = min(__popcll(sm), kSpecKeys);
         s_need[w][lane] = 0;
@@ -436,7 +512,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
           if (in_lds) s_rr[i] = rr;
           a.rowref[base + i] = rr;
           if (a.slot) {
-            const uint64_t bk = (uint64_t)s_pb[w][j] + e;
+            const uint64_t bk = (uint64_t)(s_pb[w][j] - s_tab[(s_pl[w][j] >> 3) & 1u].z) + e;
             a.slot[base + i] = rr == kMiss ? -1 : (int64_t)(bk * kKeysPerBucket) + h.l;
           }
         }
@@ -452,8 +528,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int j = r * 8 + grp;
-          const uint32_t pl = s_pl[w][j];
-          const uint64_t* bp = a.d.tab[(pl >> 3) & 1u].buckets + (uint64_t)s_pb[w][j] * kWordsPerBucket;
+          const uint64_t* bp = tabs.bucket(s_pb[w][j]);
           v[r] = *reinterpret_cast<const u64x2*>(bp + 2 * sub);
         }
 #pragma unroll
@@ -462,9 +537,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
           vs[q] = u64x2{kEmpty, kEmpty};
           if (s < nspec) {
             const int j = s_sj[w][s];
-            const uint32_t pl = s_pl[w][j];
-            const uint64_t* bp = a.d.tab[(pl >> 3) & 1u].buckets +
-                                 ((uint64_t)s_pb[w][j] + 1u) * kWordsPerBucket;
+            const uint64_t* bp = tabs.bucket(s_pb[w][j] + 1u);
             vs[q] = *reinterpret_cast<const u64x2*>(bp + 2 * sub);
           }
         }
@@ -474,42 +547,136 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
         }
         // staged values are read from LDS as each round is evaluated, not held across the loads
         asm volatile("" ::: "memory");
+        if constexpr (!VAR) {
+          // Each round's match and occupancy bits come from four ballots (bit 8g + s: lane s of
+          // group g; slots 2s and 2s + 1), and every lane keeps the byte of its own key's group,
+          // so each key is evaluated once, by the lane that staged it, instead of by all eight
+          // lanes of its group in every round.  The prefix words go through LDS.  pick() packs the
+          // four bytes of group g: match and occupancy of its even and of its odd slots.
+          auto pick = [](uint64_t mx, uint64_t my, uint64_t ox, uint64_t oy, int g) -> uint32_t {
+            const int sh = 8 * g;
+            return (uint32_t)((mx >> sh) & 0xFFu) | ((uint32_t)((my >> sh) & 0xFFu) << 8) |
+                   ((uint32_t)((ox >> sh) & 0xFFu) << 16) | ((uint32_t)((oy >> sh) & 0xFFu) << 24);
+          };
+          uint32_t hb = 0;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int j = r * 8 + grp;
-          const uint64_t key = s_pk[w][j];
-          const uint32_t pl = s_pl[w][j];
-          const int l0 = (int)(pl & 7u) + (int)((pl >> 4) & 8u);
-          const BucketHit h = eval_bucket<VAR>(a.d, v[r], key, l0, sub, grp);
-          if (key == kEmpty || h.stop || (pl >> 8) == 0u) resolve(j, key, 0u, h);
-          else if (sub == 0) s_need[w][j] = 1;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+          for (int r = 0; r < 8; ++r) {
+            const int j = r * 8 + grp;
+            const uint64_t key = s_pk[w][j];
+            const uint64_t mx = __ballot(v[r].x == key);
+            const uint64_t my = __ballot(v[r].y == key) & kSlotLanes;
+            const uint64_t ox = __ballot(v[r].x != kEmpty);
+            const uint64_t oy = __ballot(v[r].y != kEmpty) & kSlotLanes;
+            if (sub == 7) s_pref[w][0][j] = (uint32_t)v[r].y;
+            if ((lane >> 3) == r) hb = pick(mx, my, ox, oy, lane & 7);
+            asm volatile("" ::: "memory");  // one round's key read at a time
+          }
+          // the next buckets of the listed keys: lane L, listed at si, reads group si & 7 of
+          // spec round si >> 3
+          const int si = lanes_below(sm);
+          const bool spec = ((sm >> lane) & 1ull) && si < nspec;
+          uint32_t nb = 0;
 #pragma unroll
-        for (int q = 0; q < kSpecKeys / 8; ++q) {
-          if (q * 8 >= nspec) break;
-          const int s = q * 8 + grp;
-          const bool ok = s < nspec;
-          const int j = ok ? s_sj[w][s] : 0;
-          const uint64_t key = ok ? s_pk[w][j] : kEmpty;
-          const uint32_t pl = s_pl[w][j];
-          const int need = ok ? s_need[w][j] : 0;
-          const BucketHit h = eval_bucket<VAR>(a.d, vs[q], key, 0, sub, grp);
-          if (need == 1) {  // the home bucket did not end the scan
-            if (h.stop || (pl >> 8) <= 1u) {
-              resolve(j, key, 1u, h);
-              if (sub == 0) s_need[w][j] = 0;
-            } else if (sub == 0) {
-              s_need[w][j] = 2;
+          for (int q = 0; q < kSpecKeys / 8; ++q) {
+            if (q * 8 >= nspec) break;
+            const int s = q * 8 + grp;
+            const bool ok = s < nspec;
+            const int j = ok ? s_sj[w][s] : 0;
+            const uint64_t key = ok ? s_pk[w][j] : kEmpty;
+            const uint64_t mx = __ballot(vs[q].x == key);
+            const uint64_t my = __ballot(vs[q].y == key) & kSlotLanes;
+            const uint64_t ox = __ballot(vs[q].x != kEmpty);
+            const uint64_t oy = __ballot(vs[q].y != kEmpty) & kSlotLanes;
+            if (sub == 7 && ok) s_pref[w][1][j] = (uint32_t)vs[q].y;
+            if (spec && (si >> 3) == q) nb = pick(mx, my, ox, oy, si & 7);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+          // one lane per key: the home bucket from its home slot, then the early next bucket
+          const uint64_t key = s_pk[w][lane];
+          const uint32_t pl = s_pl[w][lane];
+          const uint32_t follow = pl >> 8;
+          const BitScan hs = scan_bits(hb & 0xFFu, (hb >> 8) & 0xFFu, (hb >> 16) & 0xFFu, hb >> 24,
+                                       (int)(pl & 7u) + (int)((pl >> 4) & 8u));
+          bool done = true;
+          int need = 0;
+          uint32_t e = 0u, rr = kMiss;
+          int l = hs.l;
+          if (key == kEmpty) {
+          } else if (hs.l < kKeysPerBucket) {
+            if (hs.hit) rr = s_pref[w][0][lane] + hs.below;
+          } else if (spec) {
+            const BitScan ns =
+                scan_bits(nb & 0xFFu, (nb >> 8) & 0xFFu, (nb >> 16) & 0xFFu, nb >> 24, 0);
+            e = 1u;
+            l = ns.l;
+            if (ns.l < kKeysPerBucket) {
+              if (ns.hit) rr = s_pref[w][1][lane] + ns.below;
+            } else if (follow > 1u) {
+              done = false;
+              need = 2;
+            }
+          } else if (follow > 0u) {
+            done = false;
+            need = 1;
+          }
+          s_need[w][lane] = need;
+          const int i = c0 + lane;
+          if (done && i < nk) {
+            miss += (rr == kMiss);
+            if (key != kEmpty) pst.add(e + 1u);
+            if (in_lds) s_rr[i] = rr;
+            a.rowref[base + i] = rr;
+            if (a.slot) {
+              const uint64_t bk = (uint64_t)(s_pb[w][lane] - s_tab[(pl >> 3) & 1u].z) + e;
+              a.slot[base + i] = rr == kMiss ? -1 : (int64_t)(bk * kKeysPerBucket) + l;
             }
           }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        } else {
+          // mixed widths: a hit's rank sums the row units of the occupied slots before it, so
+          // each group evaluates its bucket together (eval_bucket)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const int j = r * 8 + grp;
+            const uint64_t key = s_pk[w][j];
+            const uint32_t pl = s_pl[w][j];
+            const int l0 = (int)(pl & 7u) + (int)((pl >> 4) & 8u);
+            const BucketHit h = eval_bucket<VAR>(a.d, v[r], key, l0, sub, grp);
+            if (key == kEmpty || h.stop || (pl >> 8) == 0u) resolve(j, key, 0u, h);
+            else if (sub == 0) s_need[w][j] = 1;
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+          for (int q = 0; q < kSpecKeys / 8; ++q) {
+            if (q * 8 >= nspec) break;
+            const int s = q * 8 + grp;
+            const bool ok = s < nspec;
+            const int j = ok ? s_sj[w][s] : 0;
+            const uint64_t key = ok ? s_pk[w][j] : kEmpty;
+            const uint32_t pl = s_pl[w][j];
+            const int need = ok ? s_need[w][j] : 0;
+            const BucketHit h = eval_bucket<VAR>(a.d, vs[q], key, 0, sub, grp);
+            if (need == 1) {  // the home bucket did not end the scan
+              if (h.stop || (pl >> 8) <= 1u) {
+                resolve(j, key, 1u, h);
+                if (sub == 0) s_need[w][j] = 0;
+              } else if (sub == 0) {
+                s_need[w][j] = 2;
+              }
+            }
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      }
+}
       // further passes: the keys still unresolved (a few per chunk at load factor 0.5), listed
       // in lane order and probed eight per round in the next bucket each still needs
       while (true) {
@@ -517,7 +684,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
         const uint64_t um = __ballot(need > 0);
         if (um == 0ull) break;
         const int n = __popcll(um);
-        if (need > 0) s_list[w][__popcll(um & lt)] = lane;
+        if (need > 0) s_list[w][lanes_below(um)] = lane;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -528,9 +695,7 @@ __global__ __launch_bounds__(kBlock) void k_lookup_pool(FwdLaunch a, int gs_log2
           v[r] = u64x2{kEmpty, kEmpty};
           if (s < n) {
             const int j = s_list[w][s];
-            const uint32_t pl = s_pl[w][j];
-            const uint64_t* bp = a.d.tab[(pl >> 3) & 1u].buckets +
-                                 ((uint64_t)s_pb[w][j] + (uint64_t)s_need[w][j]) * kWordsPerBucket;
+            const uint64_t* bp = tabs.bucket(s_pb[w][j] + (uint32_t)s_need[w][j]);
             v[r] = *reinterpret_cast<const u64x2*>(bp + 2 * sub);
           }
         }

@@ -400,6 +400,8 @@ def main():
                     help="run each step as the split calls (lookup_probe, then pool_fwd on the "
                          "main stream while sparse_bwd_dedup runs on a second one, then "
                          "sparse_*_apply) instead of the two fused calls")
+    ap.add_argument("--probe", choices=("auto", "lane", "coop"), default="auto",
+                    help="bucket probe form: chosen by the bucket array's size, or forced")
     ap.add_argument("--optimizer", choices=("adagrad", "ftrl"), default="adagrad",
                     help="sparse update: Adagrad, or FTRL-Proximal (alpha = the workload's lr, "
                          f"beta {FTRL_BETA}, l1 {FTRL_L1}, l2 {FTRL_L2})")
@@ -451,8 +453,9 @@ def main():
     dims = synth.field_dims(w)
     t0 = time.perf_counter()
     ftrl = args.optimizer == "ftrl"
+    probe_flag = {"auto": 0, "lane": emb.FLAG_PROBE_LANE, "coop": emb.FLAG_PROBE_COOP}[args.probe]
     T, keys, pinned = build_table(w, extra_flags=(emb.FLAG_TRACK_TOUCHED if args.lifecycle else 0) |
-                                  (emb.FLAG_FTRL if ftrl else 0))
+                                  (emb.FLAG_FTRL if ftrl else 0) | probe_flag)
     log(f"[bench] {w.name}: {keys.size} keys, table built in {time.perf_counter() - t0:.1f}s; "
         f"arena {T.info['arena_bytes'] / 2**30:.2f} GiB")
     T.arena = torch.empty(emb.table_device_bytes(T.h), dtype=torch.uint8, device=dev)
@@ -660,7 +663,7 @@ def main():
     achieved = dom_bytes / (dom[1] / 1e3) / 1e9
     # counter traffic was measured on the fused Adagrad step without tracking: other forms run
     # other kernel instantiations
-    profiled = not (ftrl or args.lifecycle or args.split) and not args.keys
+    profiled = not (ftrl or args.lifecycle or args.split) and not args.keys and args.probe == "auto"
     traffic = load_traffic(w.name, dominant) if profiled else None
     # the whole step's counter traffic, when every kernel of the step has been measured
     counter_step = None
@@ -727,6 +730,7 @@ def main():
                    "ring": R, "mean_lookups_per_step": float(np.mean([r["nnz"] for r in ring])),
                    "mean_rows_updated_per_step": float(np.mean([r["st"]["U"] for r in ring])),
                    "calls": "split, dedup on a second stream" if args.split else "fused",
+                   "probe": args.probe,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
