@@ -121,6 +121,8 @@ typedef struct {
  *   master : fp32, same packing (fp16 tables with has_master only).  NULL: master = fp32(row).
  * Layout (ordered linear probing in 128-byte buckets of 15 keys; rows stored in slot order) is a
  * pure function of the key set.  The inputs are copied; the caller may free them on return.
+ * Size limits (EMB_ERANGE): each table at most 2^32 - 16 buckets, both tables' bucket arrays
+ * together below 2^32 buckets (512 GiB), and the rowref space below 2^32 units.
  */
 int table_create_from_prebuilt(const EmbTableDesc* desc, const int64_t* keys, int64_t n_keys,
                                const void* rows, const float* acc, const float* master,
