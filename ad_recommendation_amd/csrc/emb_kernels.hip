@@ -1028,7 +1028,6 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
   __syncthreads();
 
   uint32_t key[IPT], val[IPT], rank[IPT];
-  const uint64_t lt = (1ull << lane) - 1ull;
   // all of this thread's items first (masked-off items read item 0), then the ranking
 #pragma unroll
   for (int k = 0; k < IPT; ++k) {
@@ -1066,14 +1065,26 @@ __global__ __launch_bounds__(kBlock) void k_sort_scatter(SortArgs a) {
       }
     }
     const uint32_t dg = digit_of(kk, a.shift, a.bits);
-    uint64_t m = __ballot(valid);
-    for (int bit = 0; bit <= a.bits; ++bit) {
-      const uint64_t bb = __ballot((dg >> bit) & 1u);
-      m &= ((dg >> bit) & 1u) ? bb : ~bb;
+    // the lanes of this round whose item has the same digit: one ballot per digit bit (the miss
+    // bin's bit included), kept as two 32-bit halves; sb is all ones where this lane's bit is set,
+    // and a lane stays a peer where the ballot agrees with it
+    const uint64_t vb = __ballot(valid);
+    uint32_t mlo = (uint32_t)vb, mhi = (uint32_t)(vb >> 32);
+#pragma unroll
+    for (int bit = 0; bit <= LOGB; ++bit) {
+      if (bit <= a.bits) {
+        const int32_t top = (int32_t)(dg << (31 - bit));  // this bit in the sign position
+        const uint64_t bb = __ballot(top < 0);
+        const uint32_t sb = (uint32_t)(top >> 31);
+        mlo &= ~((uint32_t)bb ^ sb);
+        mhi &= ~((uint32_t)(bb >> 32) ^ sb);
+      }
     }
+    const uint64_t m = ((uint64_t)mhi << 32) | mlo;
+    const int below = lanes_below(m);
     const uint32_t before = s_wcnt[w][dg];
-    if (valid && (m & lt) == 0) s_wcnt[w][dg] = before + (uint32_t)__popcll(m);
-    rank[k] = before + (uint32_t)__popcll(m & lt);
+    if (valid && below == 0) s_wcnt[w][dg] = before + (uint32_t)__popcll(m);
+    rank[k] = before + (uint32_t)below;
     key[k] = kk;
     val[k] = vv;
   }
