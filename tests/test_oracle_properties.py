@@ -10,7 +10,7 @@ from gen import synth, workloads as W  # noqa: E402
 from oracle import emb_oracle as O  # noqa: E402
 from tests.test_oracle_probe_stats import brute_force  # noqa: E402
 
-FAST = settings(max_examples=60, deadline=None)
+FAST = settings(max_examples=60, deadline=None, derandomize=True, database=None)
 
 
 @st.composite
@@ -50,7 +50,7 @@ def test_scan_buckets_equal_the_walk(ks, seed, per_bucket):
                           brute_force(ot, q.view(np.int64), off, per_bucket))
 
 
-@settings(max_examples=30, deadline=None)
+@settings(max_examples=30, deadline=None, derandomize=True, database=None)
 @given(st.integers(0, 2**32 - 1), st.integers(1, 1 << 17))
 def test_dyadic_gradients_sum_exactly_in_fp32_in_any_order(seed, n):
     """Every element of synth.dyadic_grad is a multiple of 2^-7 in [-1, 1]; a sum of up to 2^17
