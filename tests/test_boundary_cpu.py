@@ -235,7 +235,7 @@ def test_bench_plan_mirrors_the_library(w):
     dims = synth.field_dims(w)
     space, classed = T.info["rowref_space"], bool(T.info["unique_by_width"])
     al = lambda x: (x + 255) & ~255  # noqa: E731
-    for nnz in (1, 1000, 325_000, 1_500_000, 5_000_000):
+    for nnz in (1, 1000, 325_000, 1_500_000, 5_000_000, 32_768_000, 50_331_648):
         ipt, tiles, bits = bench.sort_plan(nnz, space, classed)
         pw, n_pieces = bench.piece_plan(nnz, int(dims.max()), w.row_dtype == "f16", classed)
         bins = (1 << bits) + 1
